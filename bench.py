@@ -1,0 +1,477 @@
+"""Benchmark of the DCP partial-merge path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv3|longctx|split|tiny|kimi] [--B 64]
+
+Default workload: DeepSeek-V3-shaped MLA decode -- N=8 simulated DCP ranks,
+B=64 tokens, H=128 heads (16 per rank), D=512 (kv_lora_rank), bf16 partials,
+fp32 base-2 LSE, peer-outer interleaved send buffers [N,B,16,514].  One step
+is one decode step over 61 MLA layers; each layer packs all 8 ranks' send
+buffers (one launch) and combines all 8 destinations (one launch), the
+exchange between them being a zero-copy view of the stacked send buffers.
+Every layer has its own buffers (61 distinct sets, 8.6 GB), so no layer's
+inputs are cache-resident when it runs.  The step is captured once in a HIP
+graph and replayed K times; inputs are in HBM before timing starts.
+
+Printed: one JSON line with the whole-step throughput in GB/s of algorithmic
+bytes (what the method must move: (3N+1)(D*e+4) bytes per (token, head) for
+pack + combine), microseconds per layer, the roofline entry of the dominant
+kernel (per-launch duration from HIP events on the launch stream, over a
+replayed graph of that kernel's launches) and the CPU oracle timed on a
+bounded sample.
+
+Other modes:
+  --counter-run       run a 1 GiB plain copy and a few launches of each kernel
+                      (the command to put under rocprofv3 --pmc)
+  --summarize-counters DIR   turn rocprofv3 counter CSVs in DIR into
+                      profiles/counters_<workload>.json (+ a .md summary)
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "pack+LSE-combine HBM GB/s (% of MI355X peak); µs per MLA layer decode step"
+CSRC = os.path.join(ROOT, "lse_weighted_merge_dcp_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))
+                    + glob.glob(os.path.join(CSRC, "*.cpp"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+class A2AWorkload:
+    """Interleaved or split pack + combine, `layers` distinct buffer sets."""
+
+    def __init__(self, key, B, layers, dev):
+        import numpy as np
+        import torch
+
+        from lse_weighted_merge_dcp_amd import sim, synth
+
+        w = synth.WORKLOADS[key]
+        if B is not None:
+            w = w.with_batch(B)
+        self.w, self.layers, self.dev = w, layers, dev
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        t0 = time.time()
+        self.inp = synth.rank_inputs(w)
+        print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
+        o = self.inp["out"]
+        if w.dtype == "bf16":
+            o0 = torch.from_numpy(o.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            o0 = torch.from_numpy(o).to(dev)
+        l0 = torch.from_numpy(self.inp["lse"]).to(dev)
+        self.src, self.lse, self.stk, self.out, self.glse = [], [], [], [], []
+        cls = sim.StackedSplit if w.layout == "split" else sim.StackedInterleaved
+        # distinct buffer sets: one per layer while that stays under 16 GiB, else
+        # enough sets rotated that >= 2 GiB of other traffic separates two uses
+        per_layer = 2 * o0.numel() * o0.element_size() + w.N * w.B * w.Hpr * w.D * o0.element_size()
+        if per_layer * layers <= (16 << 30):
+            self.distinct = layers
+        else:
+            self.distinct = min(layers, max(4, math.ceil((2 << 30) / per_layer)))
+        for _ in range(self.distinct):
+            self.src.append(o0.clone())
+            self.lse.append(l0.clone())
+            st = cls(w.N, w.B, w.H, w.D, tdt, dev)
+            self.stk.append(st)
+            self.out.append(torch.empty((w.N, w.B, w.Hpr, w.D), dtype=tdt, device=dev))
+            self.glse.append(torch.empty((w.N, w.B, w.Hpr), dtype=torch.float32, device=dev))
+        if w.layout == "split":
+            # the exchange is a collective, not part of the merge: run it once, untimed
+            for l in range(self.distinct):
+                self.stk[l].pack(self.src[l], self.lse[l])
+                self.stk[l].exchange()
+        torch.cuda.synchronize()
+        e = w.esize
+        row = w.D * e + 4
+        per_th = w.B * w.H
+        self.bytes_pack = 2 * w.N * per_th * row            # every rank reads and writes its B*H rows
+        self.bytes_combine = w.N * per_th * row + per_th * row   # read N partials per output row, write out + G
+        self.bytes_layer = self.bytes_pack + self.bytes_combine
+        self.dtype = w.dtype
+
+    def pack(self, l):
+        k = l % self.distinct
+        self.stk[k].pack(self.src[k], self.lse[k])
+
+    def combine(self, l):
+        k = l % self.distinct
+        self.stk[k].combine(is_lse_base_on_e=not self.w.base2, out=self.out[k], out_lse=self.glse[k])
+
+    def step_launches(self):
+        fns = []
+        for l in range(self.layers):
+            fns.append(lambda l=l: self.pack(l))
+            fns.append(lambda l=l: self.combine(l))
+        return fns
+
+    def kernels(self):
+        """(name, per-launch algorithmic bytes, list of launch closures)."""
+        return [("pack", self.bytes_pack, [lambda l=l: self.pack(l) for l in range(self.layers)]),
+                ("combine", self.bytes_combine, [lambda l=l: self.combine(l) for l in range(self.layers)])]
+
+    def step_bytes(self):
+        return self.layers * self.bytes_layer
+
+    def config(self):
+        w = self.w
+        return {"workload": "%s: N=%d simulated ranks, B=%d, H=%d (%d per rank), D=%d %s, base-%s LSE, %s layout, "
+                            "%d layers per step" % (
+                                {"dsv3": "DeepSeek-V3-shaped MLA decode", "longctx": "long-context decode sweep",
+                                 "split": "peer-inside split layout", "tiny": "tiny merge"}[w.key],
+                                w.N, w.B, w.H, w.Hpr, w.D, w.dtype, "2" if w.base2 else "e", w.layout,
+                                self.layers),
+                "N": w.N, "B": w.B, "H": w.H, "D": w.D, "layers": self.layers, "layout": w.layout,
+                "distinct_buffer_sets": self.distinct}
+
+    def cpu_sample(self, budget_s):
+        """Time the oracle on whole layers of the same workload (pack of every rank
+        and combine of every destination, interleaved layout) within ~budget_s."""
+        import numpy as np
+
+        from oracle import oracle as orc
+
+        w, inp = self.w, self.inp
+        lpd = 4 // w.esize
+        npdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+        done, t_total = 0, 0.0
+        while True:
+            t0 = time.perf_counter()
+            send = np.empty((w.N, w.N, w.B, w.Hpr, w.D + lpd), npdt)
+            pay, words = orc.interleaved_views_np(send, w.D, w.dtype)
+            for r in range(w.N):
+                orc.pack(inp["out"][r], inp["lse"][r], pay[r], words[r], w.N)
+            for p in range(w.N):
+                orc.combine(pay[:, p], words[:, p], w.dtype, w.base2)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= budget_s or done >= self.layers:
+                break
+        return {"value": self.bytes_layer * done / t_total / 1e9, "unit": "GB/s", "cores": orc.num_threads(),
+                "kind": "oracle",
+                "sample": "%d whole layer(s) of the same workload (pack of all %d ranks + combine of all %d "
+                          "destinations), %.1f s of CPU time, fp64" % (done, w.N, w.N, t_total),
+                "us_per_layer": t_total / done * 1e6}
+
+
+class InplaceWorkload:
+    """The in-place merge over every rank's partial (Kimi-K3 cached-extend shape)."""
+
+    def __init__(self, B, dev):
+        import torch
+
+        from lse_weighted_merge_dcp_amd import synth
+
+        w = synth.WORKLOADS["kimi"]
+        if B is not None:
+            w = w.with_batch(B)
+        self.w, self.dev, self.layers = w, dev, 1
+        t0 = time.time()
+        self.part = synth.kimi_partial_device(w, dev)
+        self.pristine = self.part.clone()
+        self.lse_np = synth.kimi_lse(w)
+        self.lse = torch.from_numpy(self.lse_np).to(dev)
+        self.out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+        self.glse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
+        row = 4 * w.D
+        self.bytes_call = w.B * w.H * (w.N * (row + 4) + w.N * row + row + 4)
+        self.dtype = "f32"
+
+    def run(self):
+        from lse_weighted_merge_dcp_amd import ops
+
+        ops.cp_lse_combine_inplace(self.part, self.lse, out=self.out, out_lse=self.glse, return_lse=True)
+
+    def restore(self):
+        self.part.copy_(self.pristine)
+
+    def kernels(self):
+        return [("inplace", self.bytes_call, [self.run])]
+
+    def step_bytes(self):
+        return self.bytes_call
+
+    def config(self):
+        w = self.w
+        return {"workload": "Kimi-K3-shaped cached-extend in-place merge: N=8 ranks' partials [%d, %d, %d] fp32, "
+                            "base-e LSE with 0.1%% NaN/inf" % (w.B, w.H, w.D),
+                "N": w.N, "T": w.B, "H": w.H, "D": w.D}
+
+    def cpu_sample(self, budget_s):
+        import numpy as np
+
+        from oracle import oracle as orc
+
+        w = self.w
+        tblk = 64
+        done, t_total = 0, 0.0
+        while t_total < budget_s and done + tblk <= w.B:
+            part = self.pristine[:, done:done + tblk].cpu().numpy()
+            lse = self.lse_np[:, done:done + tblk]
+            t0 = time.perf_counter()
+            orc.inplace(part, lse, "f32", False)
+            t_total += time.perf_counter() - t0
+            done += tblk
+        per_tok = self.bytes_call / w.B
+        return {"value": per_tok * done / t_total / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+                "sample": "first %d of %d tokens (all 8 ranks, 96 heads), %.1f s of CPU time, fp64" % (
+                    done, w.B, t_total)}
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+def per_launch_us(launches, reps, restore=None):
+    """Average duration of one launch: a HIP graph of the given launches is
+    replayed `reps` times between two HIP events recorded on the stream the
+    kernels run on.  Returns (us per launch, graph)."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in launches:          # warm, outside the graph
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    total = 0.0
+    stream = torch.cuda.current_stream()
+    for _ in range(reps):
+        if restore is not None:
+            restore()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        total += a.elapsed_time(b) * 1e3
+    return total / (reps * len(launches)), g
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3", choices=["dsv3", "longctx", "split", "tiny", "kimi"])
+    ap.add_argument("--B", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=61)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--counter-run", action="store_true")
+    ap.add_argument("--summarize-counters", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build simulates all DCP ranks on a single MI355X "
+              "(stacked in its HBM) and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == "kimi":
+        wl = InplaceWorkload(args.B, dev)
+    else:
+        wl = A2AWorkload(args.workload, args.B, args.layers, dev)
+
+    if args.counter_run:
+        counter_run(wl)
+        return
+
+    # ---- the step: all layers, captured once in a HIP graph ----------------
+    if args.workload == "kimi":
+        step = [wl.run]
+        restore = wl.restore
+    else:
+        step = wl.step_launches()
+        restore = None
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(args.warmup, 1)):
+            if restore:
+                restore()
+            for f in step:
+                f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in step:
+            f()
+    for _ in range(args.warmup):
+        if restore:
+            restore()
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    if restore is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        # the in-place call destroys its input: restore it (untimed) before each step
+        wall = 0.0
+        for _ in range(args.steps):
+            restore()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    gbs = wl.step_bytes() / (wall / args.steps) / 1e9
+
+    # ---- per-kernel durations: HIP events around replayed graphs of one kernel
+    kinfo = {}
+    for name, nbytes, launches in wl.kernels():
+        us, _ = per_launch_us(launches, reps=max(3, args.steps // 4), restore=restore)
+        kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9}
+    dom = max(kinfo, key=lambda k: kinfo[k]["us_per_launch"])
+    achieved = kinfo[dom]["GBps"]
+    traffic = load_traffic(args.workload, wl, dom)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = wl.cpu_sample(args.cpu_budget)
+
+    layers = getattr(wl, "layers", 1)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": wl.config(),
+        "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "us_per_layer": round(ms_per_step * 1e3 / layers, 3),
+        "bytes_per_step": wl.step_bytes(),
+        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kinfo.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def counter_run(wl):
+    """For rocprofv3 --pmc: a 1 GiB plain copy (the scale reference), then
+    three launches of each kernel of the workload."""
+    import torch
+
+    n = 1 << 29
+    a = torch.ones(n, dtype=torch.bfloat16, device=wl.dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    for name, nbytes, launches in wl.kernels():
+        for f in launches[:3]:
+            if hasattr(wl, "restore"):
+                wl.restore()
+            f()
+        torch.cuda.synchronize()
+        print("# counter run: %s x3, %d algorithmic bytes per launch" % (name, nbytes), flush=True)
+
+
+def load_traffic(workload, wl, kernel):
+    p = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source") != kernel_source_hash() or kernel not in d.get("kernels", {}):
+        return None
+    return d["kernels"][kernel]["hbm_bytes_per_launch"]
+
+
+def summarize_counters(directory, workload):
+    """rocprofv3 --pmc CSVs (FETCH_SIZE run and WRITE_SIZE run) -> per-launch
+    HBM bytes of each kernel, scaled by the copy reference."""
+    import csv
+
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    by = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        cn = r.get("Counter_Name", "")
+        val = float(r.get("Counter_Value", "nan"))
+        by.setdefault((name, cn), []).append(val)
+
+    def pick(pattern, cn):
+        vals = [v for (k, c), vs in by.items() if pattern in k and c == cn for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    copy_bytes = (1 << 29) * 2
+    f_copy = pick("elementwise_kernel", "FETCH_SIZE")
+    w_copy = pick("elementwise_kernel", "WRITE_SIZE")
+    if f_copy is None or w_copy is None:
+        raise SystemExit("no copy-reference counters found in %s" % directory)
+    fs = copy_bytes / f_copy       # bytes per counter unit, from a copy of known size
+    ws = copy_bytes / w_copy
+    out = {"kernel_source": kernel_source_hash(), "workload": workload,
+           "copy_reference": {"bytes": copy_bytes, "FETCH_SIZE": f_copy, "WRITE_SIZE": w_copy,
+                              "fetch_scale": fs, "write_scale": ws}, "kernels": {}}
+    for kname, pat in (("pack", "pack_kernel"), ("combine", "combine_kernel"), ("inplace", "inplace_kernel")):
+        f = pick(pat, "FETCH_SIZE")
+        wv = pick(pat, "WRITE_SIZE")
+        if f is None or wv is None:
+            continue
+        out["kernels"][kname] = {"FETCH_SIZE": f, "WRITE_SIZE": wv, "read_bytes": f * fs, "write_bytes": wv * ws,
+                                 "hbm_bytes_per_launch": f * fs + wv * ws}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "counters_%s.json" % workload), "w") as fo:
+        json.dump(out, fo, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+if __name__ == "__main__":
+    main()

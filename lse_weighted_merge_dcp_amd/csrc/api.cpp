@@ -1,0 +1,197 @@
+// api.cpp -- the C ABI of libdcpmerge (declared in include/dcpmerge.h).
+//
+// Every check runs on the host before anything is enqueued, so a rejected
+// call has no side effect and the error paths run without a GPU.  Element
+// and word strides are turned into byte strides for the launchers.
+#include <stdint.h>
+
+#include "../../include/dcpmerge.h"
+#include "dcp_launch.hpp"
+
+namespace {
+
+using dcp::kMaxRowsPerLaunch;
+
+int esize_of(int dtype) {
+    switch (dtype) {
+        case DCP_F32: return 4;
+        case DCP_F16: return 2;
+        case DCP_BF16: return 2;
+        default: return 0;
+    }
+}
+
+bool aligned(const void* p, int a) { return ((uintptr_t)p % (uintptr_t)a) == 0; }
+
+bool nonneg(std::initializer_list<int64_t> xs) {
+    for (int64_t x : xs)
+        if (x < 0) return false;
+    return true;
+}
+
+// Shapes must keep every per-launch index within 32 bits even after the
+// launchers split the work along R, B and T.
+bool shape_fits(int64_t H, int64_t row_bytes) {
+    if (H > (int64_t(1) << 24) || row_bytes > (int64_t(1) << 28)) return false;
+    return H * (row_bytes / 32 + 1) <= kMaxRowsPerLaunch;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int dcp_lse_pack_dim(int dtype) {
+    const int e = esize_of(dtype);
+    return e == 0 ? DCP_ERR_DTYPE : 4 / e;
+}
+
+const char* dcp_status_str(int status) {
+    switch (status) {
+        case DCP_OK: return "DCP_OK";
+        case DCP_ERR_NULL: return "DCP_ERR_NULL: a required pointer is NULL";
+        case DCP_ERR_SHAPE: return "DCP_ERR_SHAPE: invalid or too large extent";
+        case DCP_ERR_HEADS_NOT_DIVISIBLE: return "DCP_ERR_HEADS_NOT_DIVISIBLE: H is not a multiple of N";
+        case DCP_ERR_DTYPE: return "DCP_ERR_DTYPE: unsupported payload dtype";
+        case DCP_ERR_LSE_BASE: return "DCP_ERR_LSE_BASE: lse_base is neither DCP_LSE_BASE_E nor DCP_LSE_BASE_2";
+        case DCP_ERR_STRIDE: return "DCP_ERR_STRIDE: negative stride";
+        case DCP_ERR_ALIGN: return "DCP_ERR_ALIGN: payload not element-aligned or LSE not 4-byte aligned";
+        case DCP_ERR_HEAD_RANGE: return "DCP_ERR_HEAD_RANGE: need 0 <= h0 < h1 <= H";
+        case DCP_ERR_LAUNCH: return "DCP_ERR_LAUNCH: HIP kernel launch failed";
+        default: return "unknown dcpmerge status";
+    }
+}
+
+int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
+             const float* src_lse, int64_t sl_R, int64_t sl_B, int64_t sl_H,
+             void* dst_o, int64_t do_R, int64_t do_N, int64_t do_B, int64_t do_H,
+             float* dst_lse, int64_t dl_R, int64_t dl_N, int64_t dl_B, int64_t dl_H,
+             int64_t R, int64_t N, int64_t B, int64_t H, int64_t D,
+             int dtype, void* stream) {
+    const int e = esize_of(dtype);
+    if (e == 0) return DCP_ERR_DTYPE;
+    if (R < 0 || B < 0 || N < 1 || H < 1 || D < 1) return DCP_ERR_SHAPE;
+    if (H % N != 0) return DCP_ERR_HEADS_NOT_DIVISIBLE;
+    if (!shape_fits(H, D * e)) return DCP_ERR_SHAPE;
+    if (!nonneg({so_R, so_B, so_H, sl_R, sl_B, sl_H, do_R, do_N, do_B, do_H, dl_R, dl_N, dl_B, dl_H}))
+        return DCP_ERR_STRIDE;
+    if (R == 0 || B == 0) return DCP_OK;
+    if (!src_o || !src_lse || !dst_o || !dst_lse) return DCP_ERR_NULL;
+    if (!aligned(src_o, e) || !aligned(dst_o, e) || !aligned(src_lse, 4) || !aligned(dst_lse, 4))
+        return DCP_ERR_ALIGN;
+    dcp::PackArgs a;
+    a.src = (const char*)src_o;
+    a.src_lse = (const char*)src_lse;
+    a.dst = (char*)dst_o;
+    a.dst_lse = (char*)dst_lse;
+    a.s_R = so_R * e; a.s_B = so_B * e; a.s_H = so_H * e;
+    a.sl_R = sl_R * 4; a.sl_B = sl_B * 4; a.sl_H = sl_H * 4;
+    a.d_R = do_R * e; a.d_N = do_N * e; a.d_B = do_B * e; a.d_H = do_H * e;
+    a.dl_R = dl_R * 4; a.dl_N = dl_N * 4; a.dl_B = dl_B * 4; a.dl_H = dl_H * 4;
+    a.R = R; a.B = B; a.H = H; a.Hpr = H / N;
+    a.row_bytes = D * e;
+    a.esize = e;
+    return launch_status(dcp::launch_pack(a, (hipStream_t)stream));
+}
+
+int dcp_unpack_combine(const void* recv_o, int64_t ro_R, int64_t ro_N, int64_t ro_B, int64_t ro_H,
+                       const float* recv_lse, int64_t rl_R, int64_t rl_N, int64_t rl_B, int64_t rl_H,
+                       void* out, int64_t oo_R, int64_t oo_B, int64_t oo_H,
+                       float* out_lse, int64_t ol_R, int64_t ol_B, int64_t ol_H,
+                       int64_t R, int64_t N, int64_t B, int64_t Hpr, int64_t D,
+                       int dtype, int lse_base, void* stream) {
+    const int e = esize_of(dtype);
+    if (e == 0) return DCP_ERR_DTYPE;
+    if (lse_base != DCP_LSE_BASE_E && lse_base != DCP_LSE_BASE_2) return DCP_ERR_LSE_BASE;
+    if (R < 0 || B < 0 || N < 1 || Hpr < 1 || D < 1) return DCP_ERR_SHAPE;
+    if (N > (int64_t(1) << 20) || !shape_fits(Hpr, D * e)) return DCP_ERR_SHAPE;
+    if (!nonneg({ro_R, ro_N, ro_B, ro_H, rl_R, rl_N, rl_B, rl_H, oo_R, oo_B, oo_H, ol_R, ol_B, ol_H}))
+        return DCP_ERR_STRIDE;
+    if (R == 0 || B == 0) return DCP_OK;
+    if (!recv_o || !recv_lse || !out) return DCP_ERR_NULL;
+    if (!aligned(recv_o, e) || !aligned(out, e) || !aligned(recv_lse, 4) || (out_lse && !aligned(out_lse, 4)))
+        return DCP_ERR_ALIGN;
+    if (N == 1) {
+        // the world_size == 1 shortcut: out and out_lse are the partial and its LSE, unchanged
+        dcp::PackArgs a;
+        a.src = (const char*)recv_o;
+        a.src_lse = (const char*)recv_lse;
+        a.dst = (char*)out;
+        a.dst_lse = (char*)out_lse;
+        a.s_R = ro_R * e; a.s_B = ro_B * e; a.s_H = ro_H * e;
+        a.sl_R = rl_R * 4; a.sl_B = rl_B * 4; a.sl_H = rl_H * 4;
+        a.d_R = oo_R * e; a.d_N = 0; a.d_B = oo_B * e; a.d_H = oo_H * e;
+        a.dl_R = ol_R * 4; a.dl_N = 0; a.dl_B = ol_B * 4; a.dl_H = ol_H * 4;
+        a.R = R; a.B = B; a.H = Hpr; a.Hpr = Hpr;
+        a.row_bytes = D * e;
+        a.esize = e;
+        return launch_status(dcp::launch_pack(a, (hipStream_t)stream));
+    }
+    dcp::CombineArgs a;
+    a.recv = (const char*)recv_o;
+    a.recv_lse = (const char*)recv_lse;
+    a.out = (char*)out;
+    a.out_lse = (char*)out_lse;
+    a.r_R = ro_R * e; a.r_N = ro_N * e; a.r_B = ro_B * e; a.r_H = ro_H * e;
+    a.rl_R = rl_R * 4; a.rl_N = rl_N * 4; a.rl_B = rl_B * 4; a.rl_H = rl_H * 4;
+    a.o_R = oo_R * e; a.o_B = oo_B * e; a.o_H = oo_H * e;
+    a.ol_R = ol_R * 4; a.ol_B = ol_B * 4; a.ol_H = ol_H * 4;
+    a.R = R; a.N = N; a.B = B; a.Hpr = Hpr; a.D = D;
+    a.dtype = dtype;
+    a.base2 = lse_base == DCP_LSE_BASE_2;
+    return launch_status(dcp::launch_combine(a, (hipStream_t)stream));
+}
+
+int dcp_lse_combine_inplace(void* partial, int64_t p_N, int64_t p_T, int64_t p_H,
+                            const float* lse, int64_t l_N, int64_t l_T, int64_t l_H,
+                            int64_t h0, int64_t h1,
+                            void* out, int64_t o_T, int64_t o_H,
+                            float* out_lse, int64_t ol_T, int64_t ol_H,
+                            int64_t N, int64_t P, int64_t rank0,
+                            int64_t T, int64_t H, int64_t D,
+                            int dtype, int lse_base, void* stream) {
+    const int e = esize_of(dtype);
+    if (e == 0) return DCP_ERR_DTYPE;
+    if (lse_base != DCP_LSE_BASE_E && lse_base != DCP_LSE_BASE_2) return DCP_ERR_LSE_BASE;
+    if (T < 0 || N < 1 || H < 1 || D < 1 || P < 1 || rank0 < 0 || rank0 + P > N) return DCP_ERR_SHAPE;
+    if (N > (int64_t(1) << 20) || !shape_fits(H, D * e)) return DCP_ERR_SHAPE;
+    if (h0 < 0 || h1 <= h0 || h1 > H) return DCP_ERR_HEAD_RANGE;
+    if (!nonneg({p_N, p_T, p_H, l_N, l_T, l_H, o_T, o_H, ol_T, ol_H})) return DCP_ERR_STRIDE;
+    if (T == 0) return DCP_OK;
+    if (!partial || !lse) return DCP_ERR_NULL;
+    if (!aligned(partial, e) || (out && !aligned(out, e)) || !aligned(lse, 4) || (out_lse && !aligned(out_lse, 4)))
+        return DCP_ERR_ALIGN;
+    if (N == 1) {
+        // the world_size == 1 shortcut: the partial stays as it is; the slice is copied
+        if (!out && !out_lse) return DCP_OK;
+        dcp::PackArgs a;
+        a.src = (const char*)partial + h0 * p_H * e;
+        a.src_lse = (const char*)lse + h0 * l_H * 4;
+        a.dst = (char*)out;
+        a.dst_lse = (char*)out_lse;
+        a.s_R = 0; a.s_B = p_T * e; a.s_H = p_H * e;
+        a.sl_R = 0; a.sl_B = l_T * 4; a.sl_H = l_H * 4;
+        a.d_R = 0; a.d_N = 0; a.d_B = o_T * e; a.d_H = o_H * e;
+        a.dl_R = 0; a.dl_N = 0; a.dl_B = ol_T * 4; a.dl_H = ol_H * 4;
+        a.R = 1; a.B = T; a.H = h1 - h0; a.Hpr = h1 - h0;
+        a.row_bytes = D * e;
+        a.esize = e;
+        return launch_status(dcp::launch_pack(a, (hipStream_t)stream));
+    }
+    dcp::InplaceArgs a;
+    a.partial = (char*)partial;
+    a.lse = (const char*)lse;
+    a.out = (char*)out;
+    a.out_lse = (char*)out_lse;
+    a.p_N = p_N * e; a.p_T = p_T * e; a.p_H = p_H * e;
+    a.l_N = l_N * 4; a.l_T = l_T * 4; a.l_H = l_H * 4;
+    a.o_T = o_T * e; a.o_H = o_H * e;
+    a.ol_T = ol_T * 4; a.ol_H = ol_H * 4;
+    a.N = N; a.P = P; a.rank0 = rank0; a.T = T; a.H = H; a.D = D; a.h0 = h0; a.h1 = h1;
+    a.dtype = dtype;
+    a.base2 = lse_base == DCP_LSE_BASE_2;
+    return launch_status(dcp::launch_inplace(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

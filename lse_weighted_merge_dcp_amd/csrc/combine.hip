@@ -1,0 +1,312 @@
+// combine.hip -- LSE-weighted merge of N received partials, out of place
+// (sglang PR #34651 report, 实现拆解 item 3 receive side; vLLM PR #41160 report,
+// 实现拆解 item 1; the nan_to_num guards of sglang PR #34213 report's excerpt).
+//
+// Per output row (r, b, hl):  G = log_beta sum_i beta^l_i,
+// w_i = nan_to_num(beta^(l_i - G)),  out = sum_i w_i * nan_to_num(o_i).
+//
+// Work mapping.  One row group of LPR lanes (16, 32 or 64) owns one output
+// row.  Inside it, every 16-lane DPP row redundantly derives G and the
+// weights: lane j loads l_j, the maximum, the special-value flags and the
+// sum of beta^(l_j - m) are reduced with row_ror DPP steps, and each lane's
+// w_j = beta^(l_j - m) / sum is broadcast to the row with row_newbcast.  The
+// payload is then streamed in 16-byte vectors: every lane loads its chunk of
+// all N peers (N loads in flight), and accumulates w_i * o_i in fp32.
+//
+// Guards cost nothing on clean data: the sum is formed from the raw values
+// and checked once per output element.  A finite sum proves every term was
+// finite, i.e. nan_to_num would have changed nothing; otherwise the wave
+// re-forms the sum from the guarded values still held in registers.
+//
+// N > 16 (or N not in {2,4,8,16}) takes the general path: lane j handles
+// peers j, j+16, ..., and each lane recomputes the weight of each peer as it
+// streams (one exp per peer per lane, negligible next to the payload).
+#include <math.h>
+
+#include "dcp_device.hpp"
+#include "dcp_launch.hpp"
+
+namespace dcp {
+namespace {
+
+struct CombK {
+    const char* recv;
+    const char* rlse;
+    char* out;
+    char* olse;
+    int64_t r_R, r_N, r_B, r_H;
+    int64_t rl_R, rl_N, rl_B, rl_H;
+    int64_t o_R, o_B, o_H;
+    int64_t ol_R, ol_B, ol_H;
+    uint32_t rows;    // R * B * Hpr in this launch
+    uint32_t N, B, Hpr;
+    uint32_t chunks;  // D * esize / V
+    uint32_t steps;   // ceil(chunks / LPR)
+    FastDiv f_Hpr, f_B;
+    int base2;
+};
+
+// Global LSE of a row from the l_j held by the 16 lanes of each DPP row
+// (lanes past N hold -inf).  Returns G; sets e = beta^(l_j - m) and s = sum e
+// when G is finite (live), else live = false and every weight is 0.
+struct LseState {
+    float G;
+    float m;
+    float s;
+    bool live;
+};
+
+__device__ __forceinline__ LseState reduce_lse(float l_max_in, int flags_in, bool base2) {
+    LseState st;
+    const int flags = row_or(flags_in);
+    const float m = row_max(l_max_in);
+    st.m = m;
+    st.s = 0.0f;
+    st.live = false;
+    if (flags & 1) {
+        st.G = __builtin_nanf("");
+    } else if (flags & 2) {
+        st.G = INFINITY;
+    } else if (m == -INFINITY) {
+        st.G = -INFINITY;
+    } else {
+        st.live = true;
+        st.G = 0.0f;  // completed by the caller once the sum is known
+    }
+    return st;
+}
+
+__device__ __forceinline__ int lse_flags(float l) {
+    return (__builtin_isnan(l) ? 1 : 0) | (l == INFINITY ? 2 : 0);
+}
+
+template <typename DT, int V, int LPR, int NT>
+__global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
+    using C = Cvt<DT, V>;
+    constexpr int EPV = C::n;
+    constexpr uint32_t RPW = 64 / LPR;
+    const uint32_t blk = xcd_block();
+    const uint32_t wave = wave_id();
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t li = lane % LPR;
+    const uint32_t g = lane / LPR;
+    const uint32_t j = lane & 15u;
+    const uint32_t row = (blk * 4u + wave) * RPW + g;
+    if (row >= k.rows) return;  // whole row groups (and so whole DPP rows) leave together
+    const bool base2 = k.base2 != 0;
+
+    const uint32_t bb = fdiv(row, k.f_Hpr);
+    const uint32_t hl = row - bb * k.Hpr;
+    const uint32_t r = fdiv(bb, k.f_B);
+    const uint32_t b = bb - r * k.B;
+    const char* rbase = k.recv + r * k.r_R + b * k.r_B + hl * k.r_H;
+    const char* lbase = k.rlse + r * k.rl_R + b * k.rl_B + hl * k.rl_H;
+    char* obase = k.out + r * k.o_R + b * k.o_B + hl * k.o_H;
+
+    if constexpr (NT > 0) {
+        // ---- fixed N <= 16: lane j of every DPP row holds peer j ----------
+        float lj = -INFINITY;
+        if (j < (uint32_t)NT) lj = load_f32(lbase + (int64_t)j * k.rl_N);
+        LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj), base2);
+        float w = 0.0f;
+        if (st.live) {
+            const float e = (j < (uint32_t)NT) ? exp_base(lj - st.m, base2) : 0.0f;
+            const float s = row_sum(e);
+            st.G = st.m + log_base(s, base2);
+            w = e / s;
+        }
+        float wi[NT];
+        [&]<int... I>(std::integer_sequence<int, I...>) { ((wi[I] = row_bcast<I>(w)), ...); }
+        (std::make_integer_sequence<int, NT>{});
+
+        for (uint32_t step = 0; step < k.steps; ++step) {
+            const uint32_t c = step * LPR + li;
+            if (c < k.chunks) {
+                const int64_t coff = (int64_t)c * V;
+                Vec<V> x[NT];
+#pragma unroll
+                for (int i = 0; i < NT; ++i) x[i] = vload<V>(rbase + i * k.r_N + coff);
+                float acc[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    float f[EPV];
+                    C::unpack(x[i], f);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], f[e], acc[e]);
+                }
+                bool bad = false;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) {
+                        float f[EPV];
+                        C::unpack(x[i], f);
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
+                    }
+                }
+                vstore<V>(obase + coff, C::pack(acc));
+            }
+        }
+        if (k.olse != nullptr && li == 0)
+            *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
+    } else {
+        // ---- any N: lane j of every DPP row covers peers j, j+16, ... -----
+        const int N = (int)k.N;
+        float lmax = -INFINITY;
+        int fl = 0;
+        for (int i = (int)j; i < N; i += 16) {
+            const float l = load_f32(lbase + i * k.rl_N);
+            fl |= lse_flags(l);
+            if (!__builtin_isnan(l)) lmax = fmaxf(lmax, l);
+        }
+        LseState st = reduce_lse(lmax, fl, base2);
+        float s = 1.0f;
+        if (st.live) {
+            float part = 0.0f;
+            for (int i = (int)j; i < N; i += 16) part += exp_base(load_f32(lbase + i * k.rl_N) - st.m, base2);
+            s = row_sum(part);
+            st.G = st.m + log_base(s, base2);
+        }
+        constexpr int PB = 8;  // peers in flight per lane
+        for (uint32_t step = 0; step < k.steps; ++step) {
+            const uint32_t c = step * LPR + li;
+            if (c < k.chunks) {
+                const int64_t coff = (int64_t)c * V;
+                float acc[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+                for (int i0 = 0; i0 < N; i0 += PB) {
+                    Vec<V> x[PB];
+                    float wv[PB];
+#pragma unroll
+                    for (int t = 0; t < PB; ++t) {
+                        const int i = i0 + t;
+                        wv[t] = 0.0f;
+                        if (i < N) {
+                            x[t] = vload<V>(rbase + i * k.r_N + coff);
+                            if (st.live) wv[t] = exp_base(load_f32(lbase + i * k.rl_N) - st.m, base2) / s;
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < PB; ++t) {
+                        if (i0 + t < N) {
+                            float f[EPV];
+                            C::unpack(x[t], f);
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wv[t], f[e], acc[e]);
+                        }
+                    }
+                }
+                bool bad = false;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+                    for (int i = 0; i < N; ++i) {
+                        const Vec<V> xv = vload<V>(rbase + i * k.r_N + coff);
+                        const float wt = st.live ? exp_base(load_f32(lbase + i * k.rl_N) - st.m, base2) / s : 0.0f;
+                        float f[EPV];
+                        C::unpack(xv, f);
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wt, guard_f(f[e]), acc[e]);
+                    }
+                }
+                vstore<V>(obase + coff, C::pack(acc));
+            }
+        }
+        if (k.olse != nullptr && li == 0)
+            *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
+    }
+}
+
+template <typename DT, int V, int LPR, int NT>
+hipError_t run(const CombineArgs& a, hipStream_t stream) {
+    constexpr int64_t RPB = 4 * (64 / LPR);
+    const int64_t chunks = a.D * DT::esize / V;
+    const int64_t steps = (chunks + LPR - 1) / LPR;
+    const int64_t per_r = a.B * a.Hpr;
+    int64_t r_chunk = per_r > 0 ? kMaxRowsPerLaunch / per_r : a.R;
+    int64_t b_chunk = a.B;
+    if (r_chunk < 1) {
+        r_chunk = 1;
+        b_chunk = kMaxRowsPerLaunch / a.Hpr;
+    }
+    for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
+        const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;
+        for (int64_t b0 = 0; b0 < a.B; b0 += b_chunk) {
+            const int64_t nb = b0 + b_chunk <= a.B ? b_chunk : a.B - b0;
+            CombK k;
+            k.recv = a.recv + r0 * a.r_R + b0 * a.r_B;
+            k.rlse = a.recv_lse + r0 * a.rl_R + b0 * a.rl_B;
+            k.out = a.out + r0 * a.o_R + b0 * a.o_B;
+            k.olse = a.out_lse ? a.out_lse + r0 * a.ol_R + b0 * a.ol_B : nullptr;
+            k.r_R = a.r_R; k.r_N = a.r_N; k.r_B = a.r_B; k.r_H = a.r_H;
+            k.rl_R = a.rl_R; k.rl_N = a.rl_N; k.rl_B = a.rl_B; k.rl_H = a.rl_H;
+            k.o_R = a.o_R; k.o_B = a.o_B; k.o_H = a.o_H;
+            k.ol_R = a.ol_R; k.ol_B = a.ol_B; k.ol_H = a.ol_H;
+            const int64_t rows = nr * nb * a.Hpr;
+            k.rows = (uint32_t)rows;
+            k.N = (uint32_t)a.N;
+            k.B = (uint32_t)nb;
+            k.Hpr = (uint32_t)a.Hpr;
+            k.chunks = (uint32_t)chunks;
+            k.steps = (uint32_t)steps;
+            k.f_Hpr = make_fastdiv(k.Hpr);
+            k.f_B = make_fastdiv(k.B);
+            k.base2 = a.base2 ? 1 : 0;
+            const int64_t blocks = (rows + RPB - 1) / RPB;
+            hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+template <typename DT, int V, int LPR>
+hipError_t run_n(const CombineArgs& a, hipStream_t stream) {
+    switch (a.N) {
+        case 2: return run<DT, V, LPR, 2>(a, stream);
+        case 4: return run<DT, V, LPR, 4>(a, stream);
+        case 8: return run<DT, V, LPR, 8>(a, stream);
+        case 16: return run<DT, V, LPR, 16>(a, stream);
+        default: return run<DT, V, LPR, 0>(a, stream);
+    }
+}
+
+template <typename DT>
+hipError_t run_dt(const CombineArgs& a, int V, hipStream_t stream) {
+    if (V == 16) {
+        const int64_t chunks = a.D * DT::esize / 16;
+        if (chunks >= 48) return run_n<DT, 16, 64>(a, stream);
+        return run_n<DT, 16, 16>(a, stream);
+    }
+    // element-granular fallback for rows that are not 16-byte multiples or
+    // not 4-byte aligned
+    return run<DT, DT::esize, 64, 0>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+    if (a.R == 0 || a.B == 0) return hipSuccess;
+    const int esize = a.dtype == DT_F32 ? 4 : 2;
+    const int64_t addrs[] = {(int64_t)(uintptr_t)a.recv, a.r_R, a.r_N, a.r_B, a.r_H,
+                             (int64_t)(uintptr_t)a.out, a.o_R, a.o_B, a.o_H};
+    int V = pick_vec_bytes(a.D * esize, esize, addrs, 9);
+    if (V != 16) V = esize;
+    switch (a.dtype) {
+        case DT_F32: return run_dt<F32T>(a, V, stream);
+        case DT_F16: return run_dt<F16T>(a, V, stream);
+        default: return run_dt<BF16T>(a, V, stream);
+    }
+}
+
+}  // namespace dcp

@@ -1,0 +1,219 @@
+// dcp_device.hpp -- device helpers shared by the pack, combine and in-place
+// kernels: vector memory access, payload conversions, 16-lane DPP row
+// reductions and broadcasts, and the XCD-aware block order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fastdiv.hpp"
+
+namespace dcp {
+
+// --------------------------------------------------------------------------
+// memory access: V-byte vectors at 4-byte (V >= 4) or 2-byte (V == 2)
+// alignment.  The payload rows of an interleaved send buffer start 4 bytes
+// apart modulo 16, so the vector types only promise dword alignment; gfx950
+// serves dword-aligned dwordx2/dwordx4 accesses directly.
+// --------------------------------------------------------------------------
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+template <int V> struct Vec;
+template <> struct Vec<16> { uint32_t w[4]; };
+template <> struct Vec<8>  { uint32_t w[2]; };
+template <> struct Vec<4>  { uint32_t w[1]; };
+template <> struct Vec<2>  { uint16_t h; };
+
+template <int V> __device__ __forceinline__ Vec<V> vload(const char* p);
+template <> __device__ __forceinline__ Vec<16> vload<16>(const char* p) {
+    u32x4_a4 x = *reinterpret_cast<const u32x4_a4*>(p);
+    Vec<16> v; v.w[0] = x.x; v.w[1] = x.y; v.w[2] = x.z; v.w[3] = x.w; return v;
+}
+template <> __device__ __forceinline__ Vec<8> vload<8>(const char* p) {
+    u32x2_a4 x = *reinterpret_cast<const u32x2_a4*>(p);
+    Vec<8> v; v.w[0] = x.x; v.w[1] = x.y; return v;
+}
+template <> __device__ __forceinline__ Vec<4> vload<4>(const char* p) {
+    Vec<4> v; v.w[0] = *reinterpret_cast<const uint32_t*>(p); return v;
+}
+template <> __device__ __forceinline__ Vec<2> vload<2>(const char* p) {
+    Vec<2> v; v.h = *reinterpret_cast<const uint16_t*>(p); return v;
+}
+
+template <int V> __device__ __forceinline__ void vstore(char* p, const Vec<V>& v);
+template <> __device__ __forceinline__ void vstore<16>(char* p, const Vec<16>& v) {
+    u32x4_a4 x; x.x = v.w[0]; x.y = v.w[1]; x.z = v.w[2]; x.w = v.w[3];
+    *reinterpret_cast<u32x4_a4*>(p) = x;
+}
+template <> __device__ __forceinline__ void vstore<8>(char* p, const Vec<8>& v) {
+    u32x2_a4 x; x.x = v.w[0]; x.y = v.w[1];
+    *reinterpret_cast<u32x2_a4*>(p) = x;
+}
+template <> __device__ __forceinline__ void vstore<4>(char* p, const Vec<4>& v) {
+    *reinterpret_cast<uint32_t*>(p) = v.w[0];
+}
+template <> __device__ __forceinline__ void vstore<2>(char* p, const Vec<2>& v) {
+    *reinterpret_cast<uint16_t*>(p) = v.h;
+}
+
+__device__ __forceinline__ uint32_t load_word(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ void store_word(char* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }
+__device__ __forceinline__ float load_f32(const char* p) { return *reinterpret_cast<const float*>(p); }
+
+// --------------------------------------------------------------------------
+// payload element types: unpack a vector to fp32 and pack fp32 back with
+// round-to-nearest-even.
+// --------------------------------------------------------------------------
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
+
+struct F32T  { static constexpr int esize = 4; };
+struct F16T  { static constexpr int esize = 2; };
+struct BF16T { static constexpr int esize = 2; };
+
+template <typename DT, int V> struct Cvt;
+
+// 32-bit payload: every word is one element.
+template <int V> struct Cvt<F32T, V> {
+    static constexpr int n = V / 4;
+    static __device__ __forceinline__ void unpack(const Vec<V>& v, float* f) {
+#pragma unroll
+        for (int k = 0; k < n; ++k) f[k] = __uint_as_float(v.w[k]);
+    }
+    static __device__ __forceinline__ Vec<V> pack(const float* f) {
+        Vec<V> v;
+#pragma unroll
+        for (int k = 0; k < n; ++k) v.w[k] = __float_as_uint(f[k]);
+        return v;
+    }
+};
+
+// 16-bit payloads, V >= 4: two elements per word, element 2k in the low half.
+template <int V> struct Cvt<F16T, V> {
+    static constexpr int n = V / 2;
+    static __device__ __forceinline__ void unpack(const Vec<V>& v, float* f) {
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k) {
+            half2v h = __builtin_bit_cast(half2v, v.w[k]);
+            f[2 * k] = (float)h.x;
+            f[2 * k + 1] = (float)h.y;
+        }
+    }
+    static __device__ __forceinline__ Vec<V> pack(const float* f) {
+        Vec<V> v;
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k) {
+            half2v h;
+            h.x = (_Float16)f[2 * k];
+            h.y = (_Float16)f[2 * k + 1];
+            v.w[k] = __builtin_bit_cast(uint32_t, h);
+        }
+        return v;
+    }
+};
+template <> struct Cvt<F16T, 2> {
+    static constexpr int n = 1;
+    static __device__ __forceinline__ void unpack(const Vec<2>& v, float* f) {
+        f[0] = (float)__builtin_bit_cast(_Float16, v.h);
+    }
+    static __device__ __forceinline__ Vec<2> pack(const float* f) {
+        Vec<2> v; v.h = __builtin_bit_cast(uint16_t, (_Float16)f[0]); return v;
+    }
+};
+
+template <int V> struct Cvt<BF16T, V> {
+    static constexpr int n = V / 2;
+    static __device__ __forceinline__ void unpack(const Vec<V>& v, float* f) {
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k) {
+            f[2 * k] = __uint_as_float(v.w[k] << 16);
+            f[2 * k + 1] = __uint_as_float(v.w[k] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ Vec<V> pack(const float* f) {
+        Vec<V> v;
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k) {
+            bf162v h;
+            h.x = (__bf16)f[2 * k];
+            h.y = (__bf16)f[2 * k + 1];
+            v.w[k] = __builtin_bit_cast(uint32_t, h);
+        }
+        return v;
+    }
+};
+template <> struct Cvt<BF16T, 2> {
+    static constexpr int n = 1;
+    static __device__ __forceinline__ void unpack(const Vec<2>& v, float* f) {
+        f[0] = __uint_as_float((uint32_t)v.h << 16);
+    }
+    static __device__ __forceinline__ Vec<2> pack(const float* f) {
+        Vec<2> v; v.h = __builtin_bit_cast(uint16_t, (__bf16)f[0]); return v;
+    }
+};
+
+// --------------------------------------------------------------------------
+// 16-lane DPP rows.  A wave64 is four DPP rows; every reduction below stays
+// inside one row and leaves the result in all 16 of its lanes.
+// --------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+// row_ror:n rotates the 16 lanes of each row right by n (DPP controls 0x121-0x12F).
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp_f<0x128>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x122>(v));
+    v = fmaxf(v, dpp_f<0x121>(v));
+    return v;
+}
+__device__ __forceinline__ int row_or(int v) {
+    v |= dpp_i<0x128>(v);
+    v |= dpp_i<0x124>(v);
+    v |= dpp_i<0x122>(v);
+    v |= dpp_i<0x121>(v);
+    return v;
+}
+// row_newbcast:i (0x150 + i, gfx90a and later) copies lane i of each row to all its lanes.
+template <int I>
+__device__ __forceinline__ float row_bcast(float v) { return dpp_f<0x150 + I>(v); }
+
+// Sum over the row.  The rotation tree adds in a different order in every
+// lane, so lane 0's total is broadcast to keep the row bit-identical.
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_f<0x128>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x122>(v);
+    v += dpp_f<0x121>(v);
+    return row_bcast<0>(v);
+}
+
+// --------------------------------------------------------------------------
+// misc
+// --------------------------------------------------------------------------
+__device__ __forceinline__ float exp_base(float x, bool base2) { return base2 ? exp2f(x) : expf(x); }
+__device__ __forceinline__ float log_base(float x, bool base2) { return base2 ? log2f(x) : logf(x); }
+__device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
+__device__ __forceinline__ float guard_f(float x) { return __builtin_isfinite(x) ? x : 0.0f; }
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block i runs on XCD
+// i mod 8), and each XCD has its own L2.  Renumber blocks so that each XCD
+// walks one contiguous range of rows: neighbouring rows share cache lines at
+// their ends (interleaved rows are 4-byte aligned), and a line stays in one L2.
+__device__ __forceinline__ uint32_t xcd_block() {
+    const uint32_t n = gridDim.x, b = blockIdx.x;
+    const uint32_t xcd = b & 7u, k = b >> 3;
+    const uint32_t q = n >> 3, rem = n & 7u;
+    return xcd * q + (xcd < rem ? xcd : rem) + k;
+}
+
+__device__ __forceinline__ uint32_t wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+}  // namespace dcp

@@ -1,0 +1,76 @@
+// dcp_launch.hpp -- internal interface between the C ABI (api.cpp) and the
+// kernel launchers.  All strides here are in BYTES; the ABI converts.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fastdiv.hpp"
+
+namespace dcp {
+
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// Pack (and the plain strided row copy the N == 1 shortcuts use):
+// for r < R, b < B, h < H with p = h / Hpr, hl = h % Hpr
+//   dst[r, p, b, hl, 0:row_bytes] = src[r, b, h, 0:row_bytes]
+//   dst_lse[r, p, b, hl]          = src_lse[r, b, h]        (if dst_lse != nullptr)
+// dst == nullptr skips the payload.
+struct PackArgs {
+    const char* src;
+    const char* src_lse;
+    char* dst;
+    char* dst_lse;
+    int64_t s_R, s_B, s_H;
+    int64_t sl_R, sl_B, sl_H;
+    int64_t d_R, d_N, d_B, d_H;
+    int64_t dl_R, dl_N, dl_B, dl_H;
+    int64_t R, B, H, Hpr;
+    int64_t row_bytes;
+    int esize;
+};
+
+// Out-of-place combine over the peer axis N (see dcp_unpack_combine).
+struct CombineArgs {
+    const char* recv;
+    const char* recv_lse;
+    char* out;
+    char* out_lse;  // nullable
+    int64_t r_R, r_N, r_B, r_H;
+    int64_t rl_R, rl_N, rl_B, rl_H;
+    int64_t o_R, o_B, o_H;
+    int64_t ol_R, ol_B, ol_H;
+    int64_t R, N, B, Hpr, D;
+    int dtype;
+    bool base2;
+};
+
+// In-place merge (see dcp_lse_combine_inplace).
+struct InplaceArgs {
+    char* partial;
+    const char* lse;
+    char* out;      // nullable
+    char* out_lse;  // nullable
+    int64_t p_N, p_T, p_H;
+    int64_t l_N, l_T, l_H;
+    int64_t o_T, o_H;
+    int64_t ol_T, ol_H;
+    int64_t N, P, rank0, T, H, D, h0, h1;
+    int dtype;
+    bool base2;
+};
+
+// Each launcher returns hipSuccess or the launch error; arguments are
+// assumed validated by the caller.
+hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_inplace(const InplaceArgs& a, hipStream_t stream);
+
+// Largest vector width (16, 8, 4 or 2 bytes) such that every row length is a
+// multiple of it and every address used is aligned to min(width, 4).
+int pick_vec_bytes(int64_t row_bytes, int esize, const int64_t* addrs_and_strides, int count);
+
+// Launches are split so that one launch never addresses more than this many
+// row-steps (keeps every in-kernel index within 32 bits).
+constexpr int64_t kMaxRowsPerLaunch = int64_t(1) << 30;
+
+}  // namespace dcp

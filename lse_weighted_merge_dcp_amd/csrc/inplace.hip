@@ -1,0 +1,276 @@
+// inplace.hip -- the in-place merge of sglang PR #34213 report (code excerpt
+// of cp_lse_ag_out_rs_mha): every held partial is overwritten with
+// nan_to_num(o) * w, and the merged row is the sum of the scaled partials
+// over the ranks, kept for the heads [h0, h1) of this rank's slice.  The page
+// does the scaling with PyTorch ops, an all-reduce and a slice copy; here one
+// pass reads each partial row once, writes it back once, and writes the slice.
+//
+// Work mapping as in combine.hip: one row group of LPR lanes per (t, h) row;
+// each 16-lane DPP row derives G and the weights of all N ranks from the
+// LSE stack with DPP reductions; the payload streams in 16-byte vectors with
+// all P held partials in flight per lane.  The fast path (P == N in
+// {2,4,8,16}, rank0 == 0: every rank stacked on this GPU) broadcasts weights
+// with row_newbcast; otherwise each lane recomputes the weight of the rank it
+// streams.  Guards as in combine.hip: a finite row sum proves every scaled
+// term finite; otherwise the terms are re-formed from guarded values.
+#include <math.h>
+
+#include "dcp_device.hpp"
+#include "dcp_launch.hpp"
+
+namespace dcp {
+namespace {
+
+struct InplK {
+    char* part;
+    const char* lse;
+    char* out;
+    char* olse;
+    int64_t p_N, p_T, p_H;
+    int64_t l_N, l_T, l_H;
+    int64_t o_T, o_H;
+    int64_t ol_T, ol_H;
+    uint32_t rows;  // T * H in this launch
+    uint32_t N, P, rank0, H, h0, h1;
+    uint32_t chunks, steps;
+    FastDiv f_H;
+    int base2;
+};
+
+__device__ __forceinline__ int lse_flags_i(float l) {
+    return (__builtin_isnan(l) ? 1 : 0) | (l == INFINITY ? 2 : 0);
+}
+
+template <typename DT, int V, int LPR, int NT>
+__global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
+    using C = Cvt<DT, V>;
+    constexpr int EPV = C::n;
+    constexpr uint32_t RPW = 64 / LPR;
+    const uint32_t blk = xcd_block();
+    const uint32_t wave = wave_id();
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t li = lane % LPR;
+    const uint32_t g = lane / LPR;
+    const uint32_t j = lane & 15u;
+    const uint32_t row = (blk * 4u + wave) * RPW + g;
+    if (row >= k.rows) return;  // whole row groups leave together
+    const bool base2 = k.base2 != 0;
+
+    const uint32_t t = fdiv(row, k.f_H);
+    const uint32_t h = row - t * k.H;
+    char* pbase = k.part + t * k.p_T + h * k.p_H;
+    const char* lbase = k.lse + t * k.l_T + h * k.l_H;
+    const bool in_slice = h >= k.h0 && h < k.h1;
+    char* obase = (k.out != nullptr && in_slice) ? k.out + t * k.o_T + (h - k.h0) * k.o_H : nullptr;
+
+    // ---- global LSE over all N ranks -------------------------------------
+    const int N = NT > 0 ? NT : (int)k.N;
+    float lmax = -INFINITY;
+    int fl = 0;
+    float lj = -INFINITY;
+    if constexpr (NT > 0) {
+        if (j < (uint32_t)NT) lj = load_f32(lbase + (int64_t)j * k.l_N);
+        fl = lse_flags_i(lj);
+        lmax = __builtin_isnan(lj) ? -INFINITY : lj;
+    } else {
+        for (int i = (int)j; i < N; i += 16) {
+            const float l = load_f32(lbase + i * k.l_N);
+            fl |= lse_flags_i(l);
+            if (!__builtin_isnan(l)) lmax = fmaxf(lmax, l);
+        }
+    }
+    fl = row_or(fl);
+    const float m = row_max(lmax);
+    float G;
+    bool live = false;
+    float s = 1.0f;
+    if (fl & 1) {
+        G = __builtin_nanf("");
+    } else if (fl & 2) {
+        G = INFINITY;
+    } else if (m == -INFINITY) {
+        G = -INFINITY;
+    } else {
+        live = true;
+        float part = 0.0f;
+        if constexpr (NT > 0) {
+            part = (j < (uint32_t)NT) ? exp_base(lj - m, base2) : 0.0f;
+        } else {
+            for (int i = (int)j; i < N; i += 16) part += exp_base(load_f32(lbase + i * k.l_N) - m, base2);
+        }
+        s = row_sum(part);
+        G = m + log_base(s, base2);
+    }
+
+    if constexpr (NT > 0) {
+        // ---- fast path: P == N == NT, rank0 == 0 --------------------------
+        const float w = (live && j < (uint32_t)NT) ? exp_base(lj - m, base2) / s : 0.0f;
+        float wi[NT];
+        [&]<int... I>(std::integer_sequence<int, I...>) { ((wi[I] = row_bcast<I>(w)), ...); }
+        (std::make_integer_sequence<int, NT>{});
+        for (uint32_t step = 0; step < k.steps; ++step) {
+            const uint32_t c = step * LPR + li;
+            if (c < k.chunks) {
+                const int64_t coff = (int64_t)c * V;
+                Vec<V> x[NT];
+#pragma unroll
+                for (int i = 0; i < NT; ++i) x[i] = vload<V>(pbase + i * k.p_N + coff);
+                float sc[NT][EPV];
+                float acc[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    C::unpack(x[i], sc[i]);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        sc[i][e] = sc[i][e] * wi[i];
+                        acc[e] += sc[i][e];
+                    }
+                }
+                bool bad = false;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) {
+                        C::unpack(x[i], sc[i]);
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) {
+                            sc[i][e] = guard_f(sc[i][e]) * wi[i];
+                            acc[e] += sc[i][e];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < NT; ++i) vstore<V>(pbase + i * k.p_N + coff, C::pack(sc[i]));
+                if (obase != nullptr) vstore<V>(obase + coff, C::pack(acc));
+            }
+        }
+    } else {
+        // ---- general path: any N, P held partials starting at rank0 -------
+        // (not the stacked-ranks hot path: the guards are applied directly)
+        const int P = (int)k.P;
+        constexpr int PB = 8;
+        for (uint32_t step = 0; step < k.steps; ++step) {
+            const uint32_t c = step * LPR + li;
+            if (c < k.chunks) {
+                const int64_t coff = (int64_t)c * V;
+                float acc[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+                for (int j0 = 0; j0 < P; j0 += PB) {
+                    Vec<V> x[PB];
+                    float wv[PB];
+#pragma unroll
+                    for (int q = 0; q < PB; ++q) {
+                        wv[q] = 0.0f;
+                        if (j0 + q < P) {
+                            x[q] = vload<V>(pbase + (j0 + q) * k.p_N + coff);
+                            if (live)
+                                wv[q] = exp_base(load_f32(lbase + (int64_t)(k.rank0 + j0 + q) * k.l_N) - m, base2) / s;
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < PB; ++q) {
+                        if (j0 + q < P) {
+                            float f[EPV];
+                            C::unpack(x[q], f);
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) {
+                                f[e] = guard_f(f[e]) * wv[q];
+                                acc[e] += f[e];
+                            }
+                            vstore<V>(pbase + (j0 + q) * k.p_N + coff, C::pack(f));
+                        }
+                    }
+                }
+                if (obase != nullptr) vstore<V>(obase + coff, C::pack(acc));
+            }
+        }
+    }
+    if (k.olse != nullptr && in_slice && li == 0)
+        *reinterpret_cast<float*>(k.olse + t * k.ol_T + (h - k.h0) * k.ol_H) = G;
+}
+
+template <typename DT, int V, int LPR, int NT>
+hipError_t run(const InplaceArgs& a, hipStream_t stream) {
+    constexpr int64_t RPB = 4 * (64 / LPR);
+    const int64_t chunks = a.D * DT::esize / V;
+    const int64_t steps = (chunks + LPR - 1) / LPR;
+    const int64_t t_chunk = kMaxRowsPerLaunch / a.H;
+    for (int64_t t0 = 0; t0 < a.T; t0 += t_chunk) {
+        const int64_t nt = t0 + t_chunk <= a.T ? t_chunk : a.T - t0;
+        InplK k;
+        k.part = a.partial + t0 * a.p_T;
+        k.lse = a.lse + t0 * a.l_T;
+        k.out = a.out ? a.out + t0 * a.o_T : nullptr;
+        k.olse = a.out_lse ? a.out_lse + t0 * a.ol_T : nullptr;
+        k.p_N = a.p_N; k.p_T = a.p_T; k.p_H = a.p_H;
+        k.l_N = a.l_N; k.l_T = a.l_T; k.l_H = a.l_H;
+        k.o_T = a.o_T; k.o_H = a.o_H;
+        k.ol_T = a.ol_T; k.ol_H = a.ol_H;
+        const int64_t rows = nt * a.H;
+        k.rows = (uint32_t)rows;
+        k.N = (uint32_t)a.N;
+        k.P = (uint32_t)a.P;
+        k.rank0 = (uint32_t)a.rank0;
+        k.H = (uint32_t)a.H;
+        k.h0 = (uint32_t)a.h0;
+        k.h1 = (uint32_t)a.h1;
+        k.chunks = (uint32_t)chunks;
+        k.steps = (uint32_t)steps;
+        k.f_H = make_fastdiv(k.H);
+        k.base2 = a.base2 ? 1 : 0;
+        const int64_t blocks = (rows + RPB - 1) / RPB;
+        hipLaunchKernelGGL((inplace_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename DT, int V, int LPR>
+hipError_t run_n(const InplaceArgs& a, hipStream_t stream) {
+    if (a.P == a.N && a.rank0 == 0) {
+        switch (a.N) {
+            case 2: return run<DT, V, LPR, 2>(a, stream);
+            case 4: return run<DT, V, LPR, 4>(a, stream);
+            case 8: return run<DT, V, LPR, 8>(a, stream);
+            case 16: return run<DT, V, LPR, 16>(a, stream);
+            default: break;
+        }
+    }
+    return run<DT, V, LPR, 0>(a, stream);
+}
+
+template <typename DT>
+hipError_t run_dt(const InplaceArgs& a, int V, hipStream_t stream) {
+    if (V == 16) {
+        const int64_t chunks = a.D * DT::esize / 16;
+        if (chunks >= 48) return run_n<DT, 16, 64>(a, stream);
+        return run_n<DT, 16, 16>(a, stream);
+    }
+    return run<DT, DT::esize, 64, 0>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_inplace(const InplaceArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int esize = a.dtype == DT_F32 ? 4 : 2;
+    int64_t addrs[] = {(int64_t)(uintptr_t)a.partial, a.p_N, a.p_T, a.p_H,
+                       (int64_t)(uintptr_t)a.out, a.o_T, a.o_H};
+    const int n = a.out ? 7 : 4;
+    int V = pick_vec_bytes(a.D * esize, esize, addrs, n);
+    if (V != 16) V = esize;
+    switch (a.dtype) {
+        case DT_F32: return run_dt<F32T>(a, V, stream);
+        case DT_F16: return run_dt<F16T>(a, V, stream);
+        default: return run_dt<BF16T>(a, V, stream);
+    }
+}
+
+}  // namespace dcp

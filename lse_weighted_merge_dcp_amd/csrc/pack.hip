@@ -1,0 +1,171 @@
+// pack.hip -- stride-driven pack of rank-local partials into per-peer send
+// layouts (sglang PR #34651 report, 实现拆解 items 1-3).  The same kernel is
+// the strided row copy behind the N == 1 shortcuts of the merge entry points.
+//
+// Work mapping.  A "row" is one (r, b, h) payload row of row_bytes bytes,
+// cut into V-byte chunks.  A row group of LPR lanes (16, 32 or 64) covers
+// LPR consecutive chunks of one row per step; rows longer than LPR*V take
+// several steps ("virtual rows" = rows x steps).  A 256-thread block runs
+// 4 waves x (64/LPR) row groups x U virtual rows, all U loads in flight
+// before the U stores.  With LPR = 64 a virtual row is wave-uniform, so its
+// index arithmetic runs on the scalar unit.  Each payload byte is read once
+// and written once; the LSE word rides along with chunk 0 of step 0.
+#include "dcp_device.hpp"
+#include "dcp_launch.hpp"
+
+namespace dcp {
+namespace {
+
+struct PackK {
+    const char* src;
+    const char* src_lse;
+    char* dst;
+    char* dst_lse;
+    int64_t s_R, s_B, s_H;
+    int64_t sl_R, sl_B, sl_H;
+    int64_t d_R, d_N, d_B, d_H;
+    int64_t dl_R, dl_N, dl_B, dl_H;
+    uint32_t vrows;   // rows * steps in this launch
+    uint32_t steps;   // ceil(chunks / LPR)
+    uint32_t chunks;  // row_bytes / V
+    uint32_t H, B, Hpr;
+    FastDiv f_steps, f_H, f_B, f_Hpr;
+};
+
+constexpr int kPackU = 4;
+
+template <int V, int LPR, int U>
+__global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
+    constexpr uint32_t RPW = 64 / LPR;
+    const uint32_t blk = xcd_block();
+    const uint32_t wave = wave_id();
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t li = lane % LPR;
+    const uint32_t g = lane / LPR;
+
+    Vec<V> v[U];
+    char* dp[U];
+    uint32_t lw[U];
+    char* dlp[U];
+    bool pl[U], ll[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        pl[u] = false;
+        ll[u] = false;
+        const uint32_t vrow = (blk * (uint32_t)U + (uint32_t)u) * (4u * RPW) + wave * RPW + g;
+        if (vrow < k.vrows) {
+            const uint32_t row = (k.steps == 1) ? vrow : fdiv(vrow, k.f_steps);
+            const uint32_t step = vrow - row * k.steps;
+            const uint32_t rb = fdiv(row, k.f_H);
+            const uint32_t h = row - rb * k.H;
+            const uint32_t r = fdiv(rb, k.f_B);
+            const uint32_t b = rb - r * k.B;
+            const uint32_t p = fdiv(h, k.f_Hpr);
+            const uint32_t hl = h - p * k.Hpr;
+            const uint32_t c = step * LPR + li;
+            if (k.dst != nullptr && c < k.chunks) {
+                const char* sp = k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V;
+                v[u] = vload<V>(sp);
+                dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + hl * k.d_H + (int64_t)c * V;
+                pl[u] = true;
+            }
+            if (k.dst_lse != nullptr && step == 0 && li == 0) {
+                lw[u] = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H);
+                dlp[u] = k.dst_lse + r * k.dl_R + p * k.dl_N + b * k.dl_B + hl * k.dl_H;
+                ll[u] = true;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (pl[u]) vstore<V>(dp[u], v[u]);
+        if (ll[u]) store_word(dlp[u], lw[u]);
+    }
+}
+
+template <int V, int LPR>
+hipError_t run(const PackArgs& a, hipStream_t stream) {
+    constexpr int64_t RPB = 4 * (64 / LPR) * kPackU;
+    const int64_t chunks = a.dst ? a.row_bytes / V : 1;
+    const int64_t steps = (chunks + LPR - 1) / LPR;
+    const int64_t per_r = a.B * a.H * steps;
+    // split along R, then along B, so one launch stays within 32-bit indices
+    int64_t r_chunk = per_r > 0 ? kMaxRowsPerLaunch / per_r : a.R;
+    int64_t b_chunk = a.B;
+    if (r_chunk < 1) {
+        r_chunk = 1;
+        b_chunk = kMaxRowsPerLaunch / (a.H * steps);
+    }
+    for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
+        const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;
+        for (int64_t b0 = 0; b0 < a.B; b0 += b_chunk) {
+            const int64_t nb = b0 + b_chunk <= a.B ? b_chunk : a.B - b0;
+            PackK k;
+            k.src = a.src ? a.src + r0 * a.s_R + b0 * a.s_B : nullptr;
+            k.src_lse = a.src_lse ? a.src_lse + r0 * a.sl_R + b0 * a.sl_B : nullptr;
+            k.dst = a.dst ? a.dst + r0 * a.d_R + b0 * a.d_B : nullptr;
+            k.dst_lse = a.dst_lse ? a.dst_lse + r0 * a.dl_R + b0 * a.dl_B : nullptr;
+            k.s_R = a.s_R; k.s_B = a.s_B; k.s_H = a.s_H;
+            k.sl_R = a.sl_R; k.sl_B = a.sl_B; k.sl_H = a.sl_H;
+            k.d_R = a.d_R; k.d_N = a.d_N; k.d_B = a.d_B; k.d_H = a.d_H;
+            k.dl_R = a.dl_R; k.dl_N = a.dl_N; k.dl_B = a.dl_B; k.dl_H = a.dl_H;
+            const int64_t vrows = nr * nb * a.H * steps;
+            k.vrows = (uint32_t)vrows;
+            k.steps = (uint32_t)steps;
+            k.chunks = (uint32_t)chunks;
+            k.H = (uint32_t)a.H;
+            k.B = (uint32_t)nb;
+            k.Hpr = (uint32_t)a.Hpr;
+            k.f_steps = make_fastdiv(k.steps);
+            k.f_H = make_fastdiv(k.H);
+            k.f_B = make_fastdiv(k.B);
+            k.f_Hpr = make_fastdiv(k.Hpr);
+            const int64_t blocks = (vrows + RPB - 1) / RPB;
+            hipLaunchKernelGGL((pack_kernel<V, LPR, kPackU>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+template <int V>
+hipError_t run_v(const PackArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.row_bytes / V;
+    if (chunks >= 48) return run<V, 64>(a, stream);
+    if (chunks > 16) return run<V, 32>(a, stream);
+    return run<V, 16>(a, stream);
+}
+
+}  // namespace
+
+int pick_vec_bytes(int64_t row_bytes, int esize, const int64_t* addrs, int count) {
+    static const int widths[4] = {16, 8, 4, 2};
+    for (int w : widths) {
+        if (w < esize) continue;
+        if (row_bytes % w != 0) continue;
+        const int64_t align = w < 4 ? w : 4;
+        bool ok = true;
+        for (int i = 0; i < count; ++i) ok = ok && (addrs[i] % align == 0);
+        if (ok) return w;
+    }
+    return esize;
+}
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
+    if (a.R == 0 || a.B == 0) return hipSuccess;
+    int V = 4;
+    if (a.dst != nullptr) {
+        const int64_t addrs[] = {(int64_t)(uintptr_t)a.src, a.s_R, a.s_B, a.s_H,
+                                 (int64_t)(uintptr_t)a.dst, a.d_R, a.d_N, a.d_B, a.d_H};
+        V = pick_vec_bytes(a.row_bytes, a.esize, addrs, 9);
+    }
+    switch (V) {
+        case 16: return run_v<16>(a, stream);
+        case 8: return run_v<8>(a, stream);
+        case 4: return run_v<4>(a, stream);
+        default: return run_v<2>(a, stream);
+    }
+}
+
+}  // namespace dcp

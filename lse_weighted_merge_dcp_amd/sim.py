@@ -1,0 +1,77 @@
+"""Single-GPU simulation of a DCP group: all N ranks stacked in one GPU's memory.
+
+The exchange between pack and combine (an all-to-all across ranks) is not a
+step of this library; here it is simulated without a second GPU:
+
+* interleaved (pynccl-style) layout: every source's send buffer
+  [N, B, Hpr, D + lpd] lives in one allocation send[src, peer, ...].  After
+  the all-to-all, destination p holds chunk p of every source, which is the
+  zero-copy view send[:, p]; all destinations together are send.transpose(0, 1).
+* split (FlashInfer-style) layout: partial_o [B, Hpr, N, D] and stats
+  [B, Hpr, N, 2] per rank, peer axis inside the heads.  The exchange moves
+  o_out[dst, b, hl, src] = partial_o[src, b, hl, dst] (stats slot 1 as opaque
+  bytes); it is simulated with a device copy that stands in for the
+  collective and is never timed as part of the merge.
+
+sglang PR #34651 report, 实现拆解 items 2-3 (both layouts and their views).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class StackedInterleaved:
+    """Peer-outer interleaved send buffers of N ranks, stacked."""
+
+    def __init__(self, N: int, B: int, H: int, D: int, dtype: torch.dtype, device):
+        assert H % N == 0
+        self.N, self.B, self.H, self.D = N, B, H, D
+        self.lpd = ops.lse_pack_dim(dtype)
+        self.send = torch.empty((N, N, B, H // N, D + self.lpd), dtype=dtype, device=device)
+        self.payload, self.words = ops.interleaved_views(self.send, D)
+
+    def pack(self, out: torch.Tensor, lse: torch.Tensor) -> None:
+        """out [N,B,H,D], lse [N,B,H]: every rank packs its own send buffer (one launch)."""
+        ops.dcp_pack_a2a_send(out, lse, self.payload, self.words)
+
+    def recv(self):
+        """Received buffers of all destinations: [dst, src, B, Hpr, D] and [dst, src, B, Hpr]."""
+        return self.payload.transpose(0, 1), self.words.transpose(0, 1)
+
+    def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None):
+        ro, rl = self.recv()
+        return ops.dcp_lse_combine(ro, rl, is_lse_base_on_e=is_lse_base_on_e, return_lse=return_lse,
+                                   out=out, out_lse=out_lse)
+
+
+class StackedSplit:
+    """FlashInfer-shaped split buffers of N ranks, stacked."""
+
+    def __init__(self, N: int, B: int, H: int, D: int, dtype: torch.dtype, device):
+        assert H % N == 0
+        Hpr = H // N
+        self.N, self.B, self.H, self.D = N, B, H, D
+        self.partial_o = torch.empty((N, B, Hpr, N, D), dtype=dtype, device=device)
+        self.stats = torch.empty((N, B, Hpr, N, 2), dtype=torch.float32, device=device)
+        self.o_out = torch.empty_like(self.partial_o)
+        self.stats_out = torch.empty_like(self.stats)
+
+    def pack(self, out: torch.Tensor, lse: torch.Tensor) -> None:
+        ops.dcp_pack_a2a_send(out, lse, self.partial_o.permute(0, 3, 1, 2, 4),
+                              self.stats[..., 0].permute(0, 3, 1, 2))
+
+    def exchange(self) -> None:
+        """Stand-in for the all-to-all: o_out[dst, b, hl, src] = partial_o[src, b, hl, dst]."""
+        self.o_out.copy_(self.partial_o.permute(3, 1, 2, 0, 4))
+        self.stats_out.copy_(self.stats.permute(3, 1, 2, 0, 4))
+
+    def recv(self):
+        """Strided receive views [dst, src, B, Hpr, D] and [dst, src, B, Hpr] (no copy)."""
+        return self.o_out.permute(0, 3, 1, 2, 4), self.stats_out[..., 0].permute(0, 3, 1, 2)
+
+    def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None):
+        ro, rl = self.recv()
+        return ops.dcp_lse_combine(ro, rl, is_lse_base_on_e=is_lse_base_on_e, return_lse=return_lse,
+                                   out=out, out_lse=out_lse)

@@ -1,0 +1,101 @@
+"""Shared helpers of the GPU tests: host<->device moves of payload arrays and
+the acceptance checks against the oracle.
+
+Tolerances (the bar stated for this path):
+  combine / in-place outputs:  |got - ref| <= tau_T * M + floor_T, with
+      M = sum_i w_i |nan_to_num(o_i)| (fp64, from the oracle) and tau_T =
+      1e-5 (fp32), 2^-7 (bf16), 2^-10 (fp16); floor_T is half the spacing of
+      T's subnormals (output rounding of tiny values).  M == 0 requires got == 0.
+  scaled partials (in-place):  |got - ref| <= tau_T * |ref| + floor_T.
+  global LSE:  same class (NaN / +inf / -inf) when the reference is not
+      finite; otherwise |got - ref| <= 1e-5 + ulp_fp32(ref): 1e-5 absolute
+      plus the fp32 rounding of G itself, which only matters for |G| > 64.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+TAU = {"f32": 1e-5, "bf16": 2.0 ** -7, "f16": 2.0 ** -10}
+FLOOR = {"f32": 2.0 ** -150, "bf16": 2.0 ** -134, "f16": 2.0 ** -25}
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+NP_DT = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+
+
+def to_dev(a: np.ndarray, dt: str, dev) -> torch.Tensor:
+    """Storage array (bf16 as uint16 bits) -> device tensor of the payload type."""
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_host(t: torch.Tensor, dt: str) -> np.ndarray:
+    """Device tensor -> storage array (bf16 as uint16 bits)."""
+    t = t.detach().cpu()
+    if dt == "bf16":
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
+
+
+def bytes_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy() if t.dtype != torch.uint8 else t.cpu().numpy()
+
+
+def decode(a: np.ndarray, dt: str) -> np.ndarray:
+    if dt == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def check_out(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, dt: str, what: str = "out") -> None:
+    got = np.asarray(got, np.float64)
+    tol = TAU[dt] * mag + FLOOR[dt]
+    err = np.abs(got - ref)
+    bad = ~(err <= tol)
+    zero = mag == 0
+    bad |= zero & (got != 0)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d elements out of tolerance (tau=%g); first %s: got %s ref %s mag %s" % (
+            what, int(bad.sum()), bad.size, TAU[dt], idx.tolist(),
+            [got[tuple(i)] for i in idx], [ref[tuple(i)] for i in idx], [mag[tuple(i)] for i in idx]))
+
+
+def check_scaled(got: np.ndarray, ref: np.ndarray, dt: str) -> None:
+    got = np.asarray(got, np.float64)
+    bad = ~(np.abs(got - ref) <= TAU[dt] * np.abs(ref) + FLOOR[dt])
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("scaled partial: %d bad; first %s got %s ref %s" % (
+            int(bad.sum()), idx.tolist(), [got[tuple(i)] for i in idx], [ref[tuple(i)] for i in idx]))
+
+
+def ulp32(x: np.ndarray) -> np.ndarray:
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 23)
+
+
+def check_lse(got: np.ndarray, ref: np.ndarray) -> None:
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nan_r, nan_g = np.isnan(ref), np.isnan(got)
+    assert np.array_equal(nan_r, nan_g), "NaN class of G differs at %s" % np.argwhere(nan_r != nan_g)[:5].tolist()
+    inf_r = np.isinf(ref)
+    assert np.array_equal(got[inf_r], ref[inf_r]), "infinite G differs"
+    assert not np.isinf(got[~inf_r & ~nan_r]).any(), "G infinite where the reference is finite"
+    fin = np.isfinite(ref)
+    err = np.abs(got[fin] - ref[fin])
+    tol = 1e-5 + ulp32(ref[fin])
+    if not np.all(err <= tol):
+        i = int(np.argmax(err - tol))
+        raise AssertionError("G off by %g (tol %g) at value %r" % (err[i], tol[i], ref[fin][i]))
+
+
+def say(*a) -> None:
+    print(*a, flush=True)
+
+
+def finite_frac(x) -> float:
+    return float(np.isfinite(x).mean()) if np.size(x) else math.nan

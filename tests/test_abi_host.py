@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI (no GPU, no kernel launch).
+
+* the shared library loads and exports every function include/dcpmerge.h declares;
+* dcp_lse_pack_dim and dcp_status_str;
+* every validation error is returned before anything is enqueued (the calls
+  below use fake, never-dereferenced addresses; only rejected or zero-sized
+  calls are made, so no kernel is launched);
+* the fast-division helper the kernels index with, compiled for the host.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from lse_weighted_merge_dcp_amd import _lib, ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcpmerge.h")
+CSRC = os.path.join(ROOT, "lse_weighted_merge_dcp_amd", "csrc")
+
+OK, NULL, SHAPE, HEADS, DTYPE, BASE, STRIDE, ALIGN, HRANGE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+A = 0x100000  # fake 256-aligned address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dcp_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["dcp_lse_combine_inplace", "dcp_lse_pack_dim", "dcp_pack",
+                                    "dcp_status_str", "dcp_unpack_combine"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r" T (\w+)$", out.stdout, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+        assert name in _lib.SIGNATURES
+
+
+def test_lse_pack_dim_and_status_strings():
+    lib = _lib.lib()
+    assert lib.dcp_lse_pack_dim(0) == 1
+    assert lib.dcp_lse_pack_dim(1) == 2
+    assert lib.dcp_lse_pack_dim(2) == 2
+    assert lib.dcp_lse_pack_dim(3) == DTYPE
+    assert lib.dcp_lse_pack_dim(-1) == DTYPE
+    for code, name in _lib.STATUS.items():
+        assert lib.dcp_status_str(code).decode().startswith(name)
+    assert ops.lse_pack_dim(torch.float16) == 2
+    with pytest.raises(ValueError):
+        ops.lse_pack_dim(torch.float64)
+
+
+def pack(**kw):
+    args = dict(src_o=A, so_R=0, so_B=512, so_H=64, src_lse=A, sl_R=0, sl_B=8, sl_H=1,
+                dst_o=A, do_R=0, do_N=256, do_B=128, do_H=64, dst_lse=A, dl_R=0, dl_N=4, dl_B=2, dl_H=1,
+                R=1, N=2, B=4, H=8, D=64, dtype=0, stream=None)
+    args.update(kw)
+    return _lib.lib().dcp_pack(*args.values())
+
+
+def combine(**kw):
+    args = dict(recv_o=A, ro_R=0, ro_N=4096, ro_B=256, ro_H=64, recv_lse=A, rl_R=0, rl_N=16, rl_B=4, rl_H=1,
+                out=A, oo_R=0, oo_B=256, oo_H=64, out_lse=A, ol_R=0, ol_B=4, ol_H=1,
+                R=1, N=2, B=4, Hpr=4, D=64, dtype=0, lse_base=0, stream=None)
+    args.update(kw)
+    return _lib.lib().dcp_unpack_combine(*args.values())
+
+
+def inplace(**kw):
+    args = dict(partial=A, p_N=8192, p_T=512, p_H=64, lse=A, l_N=32, l_T=8, l_H=1, h0=0, h1=4,
+                out=A, o_T=256, o_H=64, out_lse=A, ol_T=4, ol_H=1, N=2, P=2, rank0=0, T=4, H=8, D=64,
+                dtype=0, lse_base=0, stream=None)
+    args.update(kw)
+    return _lib.lib().dcp_lse_combine_inplace(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(N=0), SHAPE), (dict(H=0), SHAPE), (dict(D=0), SHAPE), (dict(B=-1), SHAPE), (dict(R=-1), SHAPE),
+    (dict(N=3), HEADS), (dict(N=16), HEADS),
+    (dict(so_H=-1), STRIDE), (dict(dl_N=-4), STRIDE), (dict(do_R=-1), STRIDE),
+    (dict(src_o=None), NULL), (dict(dst_lse=None), NULL),
+    (dict(src_lse=A + 2), ALIGN), (dict(dst_o=A + 1, dtype=1), ALIGN), (dict(dst_o=A + 2, dtype=0), ALIGN),
+    (dict(H=1 << 25, N=1), SHAPE), (dict(D=1 << 27), SHAPE),
+    (dict(B=0), OK), (dict(R=0), OK), (dict(B=0, src_o=None), OK),
+])
+def test_pack_validation(kw, code):
+    assert pack(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), DTYPE), (dict(lse_base=2), BASE), (dict(lse_base=-1), BASE),
+    (dict(N=0), SHAPE), (dict(Hpr=0), SHAPE), (dict(D=0), SHAPE), (dict(B=-2), SHAPE), (dict(N=1 << 21), SHAPE),
+    (dict(ro_N=-1), STRIDE), (dict(ol_B=-4), STRIDE),
+    (dict(recv_o=None), NULL), (dict(out=None), NULL), (dict(recv_lse=None), NULL),
+    (dict(recv_lse=A + 1), ALIGN), (dict(out_lse=A + 2), ALIGN), (dict(out=A + 1, dtype=2), ALIGN),
+    (dict(B=0), OK), (dict(R=0, out=None), OK),
+])
+def test_combine_validation(kw, code):
+    assert combine(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), DTYPE), (dict(lse_base=5), BASE),
+    (dict(P=0), SHAPE), (dict(P=3), SHAPE), (dict(rank0=1), SHAPE), (dict(rank0=-1), SHAPE), (dict(T=-1), SHAPE),
+    (dict(h0=-1), HRANGE), (dict(h0=4, h1=4), HRANGE), (dict(h1=9), HRANGE), (dict(h0=5, h1=3), HRANGE),
+    (dict(p_T=-1), STRIDE), (dict(ol_H=-1), STRIDE),
+    (dict(partial=None), NULL), (dict(lse=None), NULL),
+    (dict(partial=A + 2), ALIGN), (dict(lse=A + 3), ALIGN), (dict(out=A + 2), ALIGN),
+    (dict(T=0), OK),
+])
+def test_inplace_validation(kw, code):
+    assert inplace(**kw) == code
+
+
+def test_binding_rejects_host_tensors_and_bad_layouts():
+    out = torch.zeros(2, 8, 64)
+    lse = torch.zeros(2, 8)
+    with pytest.raises(ValueError):
+        ops.dcp_pack_a2a_send(out, lse, torch.zeros(2, 2, 4, 64), torch.zeros(2, 2, 4))
+    with pytest.raises(ValueError):
+        ops.dcp_lse_combine(torch.zeros(2, 2, 4, 64), torch.zeros(2, 2, 4))
+    with pytest.raises(ValueError):
+        ops.cp_lse_combine_inplace(torch.zeros(2, 2, 4, 64), torch.zeros(2, 2, 4))
+    send = torch.zeros(2, 2, 4, 66, dtype=torch.bfloat16)
+    pay, words = ops.interleaved_views(send, 64)
+    assert pay.shape == (2, 2, 4, 64) and words.shape == (2, 2, 4) and words.dtype == torch.float32
+    assert words.stride() == (2 * 4 * 33, 4 * 33, 33)
+    with pytest.raises(ValueError):
+        ops.interleaved_views(torch.zeros(2, 2, 4, 65, dtype=torch.bfloat16), 63)
+
+
+FASTDIV_TEST = r"""
+#include <cstdio>
+#include <cstdint>
+#include <random>
+#include "fastdiv.hpp"
+int main() {
+    std::mt19937_64 g(1);
+    const uint32_t ds[] = {1u, 2u, 3u, 5u, 7u, 12u, 16u, 96u, 127u, 128u, 129u, 1000u, 4096u, 65535u, 65536u,
+                           16777217u, 0x7fffffffu, 0x80000000u, 0x80000001u, 0xfffffffeu, 0xffffffffu};
+    long bad = 0;
+    for (uint32_t d : ds) {
+        dcp::FastDiv f = dcp::make_fastdiv(d);
+        const uint32_t edge[] = {0u, 1u, d - 1u, d, d + 1u, 2u * d - 1u, 0x7fffffffu, 0x80000000u, 0xfffffffeu, 0xffffffffu};
+        for (uint32_t n : edge) bad += dcp::fdiv(n, f) != n / d;
+        for (int i = 0; i < 200000; ++i) { uint32_t n = (uint32_t)g(); bad += dcp::fdiv(n, f) != n / d; }
+    }
+    for (int i = 0; i < 2000; ++i) {
+        uint32_t d = (uint32_t)g() >> (g() % 32); if (d == 0) d = 1;
+        dcp::FastDiv f = dcp::make_fastdiv(d);
+        for (int k = 0; k < 500; ++k) { uint32_t n = (uint32_t)g(); bad += dcp::fdiv(n, f) != n / d; }
+    }
+    std::printf("%ld\n", bad);
+    return bad != 0;
+}
+"""
+
+
+def test_fastdiv_matches_integer_division(tmp_path):
+    src = tmp_path / "fd.cpp"
+    src.write_text(FASTDIV_TEST)
+    exe = str(tmp_path / "fd")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-I" + CSRC, str(src), "-o", exe])
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout

@@ -1,0 +1,134 @@
+"""GPU parity of dcp_lse_combine_inplace against the fp64 oracle, including
+the full-size in-place workload (8 ranks x [16384, 96, 512] fp32 = 24 GiB)
+checked on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+from lse_weighted_merge_dcp_amd import ops, synth
+from oracle import oracle as orc
+
+from helpers import check_lse, check_out, check_scaled, decode, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def kimi_small(T):
+    w = synth.WORKLOADS["kimi"].with_batch(T)
+    return w, synth.rank_inputs(w)
+
+
+@pytest.mark.parametrize("T", [48, 5])
+def test_inplace_kimi_shape_small_T(T):
+    """The in-place workload's shape and LSE law at a small token count:
+    N=8 ranks, H=96, D=512 fp32, base e, 0.1% NaN/+inf/-inf LSE entries."""
+    w, inp = kimi_small(T)
+    say("inplace kimi T=%d" % T)
+    lse = inp["lse"].copy()
+    if T == 5:                       # plant every special value at least once
+        lse[0, 0, 0] = np.nan; lse[3, 1, 2] = np.inf; lse[:, 2, 3] = -np.inf; lse[5, 4, 95] = -np.inf
+    part = torch.from_numpy(inp["out"]).to(DEV)
+    l = torch.from_numpy(lse).to(DEV)
+    H = w.H
+    for r in (0, 3, 7):   # each simulated rank's head slice, then the full merge
+        h0, h1 = 12 * r, 12 * r + 12
+        p = part.clone()
+        out, g = ops.cp_lse_combine_inplace(p, l, h0=h0, h1=h1, return_lse=True)
+        scaled, ref, gr, mag = orc.inplace(inp["out"], lse, "f32", False, h0=h0, h1=h1)
+        check_out(out.cpu().numpy(), ref, mag, "f32", "slice %d" % r)
+        check_lse(g.cpu().numpy(), gr)
+        check_scaled(p.cpu().numpy(), scaled, "f32")
+    out = ops.cp_lse_combine_inplace(part, l, h0=0, h1=H)
+    scaled, ref, gr, mag = orc.inplace(inp["out"], lse, "f32", False)
+    check_out(out.cpu().numpy(), ref, mag, "f32", "full")
+    check_scaled(part.cpu().numpy(), scaled, "f32")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("N,P,rank0", [(8, 8, 0), (4, 1, 2), (8, 3, 5), (3, 3, 0), (17, 17, 0), (17, 2, 7), (2, 2, 0), (16, 16, 0)])
+def test_inplace_held_subsets_and_dtypes(dt, N, P, rank0):
+    """P of the N ranks' partials held (rank0 .. rank0+P-1): the single-rank
+    case P = 1 is what one GPU of a real group runs before its all-reduce."""
+    say("inplace subset", dt, N, P, rank0)
+    T, H, D = 6, 10, 192
+    g = torch.Generator().manual_seed(N * 31 + P)
+    part = synth.to_storage(torch.randn(P, T, H, D, generator=g), dt)
+    part[0, 1, 2, 5] = synth.to_storage(torch.tensor([float("nan")]), dt)[0]
+    lse = np.random.default_rng(N).normal(1, 3, size=(N, T, H)).astype(np.float32)
+    lse[rank0, 2, 4] = np.nan
+    lse[:, 3, 5] = -np.inf
+    base2 = (N + P) % 2 == 0
+    h0, h1 = 3, 8
+    p = to_dev(part, dt, DEV)
+    out, gg = ops.cp_lse_combine_inplace(p, torch.from_numpy(lse).to(DEV), h0=h0, h1=h1, rank0=rank0,
+                                         is_lse_base_on_e=not base2, return_lse=True)
+    scaled, ref, gr, mag = orc.inplace(part, lse, dt, base2, rank0=rank0, h0=h0, h1=h1)
+    check_out(decode(to_host(out, dt), dt), ref, mag, dt)
+    check_lse(gg.cpu().numpy(), gr)
+    check_scaled(decode(to_host(p, dt), dt), scaled, dt)
+
+
+def test_inplace_scale_only_and_single_rank():
+    rng = np.random.default_rng(3)
+    part = rng.normal(size=(4, 3, 6, 64)).astype(np.float32)
+    lse = rng.normal(size=(4, 3, 6)).astype(np.float32)
+    p = torch.from_numpy(part).to(DEV)
+    r = ops.cp_lse_combine_inplace(p, torch.from_numpy(lse).to(DEV), want_out=False)
+    assert r is None
+    scaled, _, _, _ = orc.inplace(part, lse, "f32", False)
+    check_scaled(p.cpu().numpy(), scaled, "f32")
+    # N == 1: the partial is left as it is and the slice is a bit copy
+    one = part[:1].copy()
+    one[0, 0, 0, 0] = np.nan
+    p1 = torch.from_numpy(one).to(DEV)
+    out, g = ops.cp_lse_combine_inplace(p1, torch.from_numpy(lse[:1]).to(DEV), h0=1, h1=4, return_lse=True)
+    assert np.array_equal(p1.cpu().numpy().view(np.uint32), one.view(np.uint32))
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), one[0][:, 1:4].view(np.uint32))
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), lse[0][:, 1:4].view(np.uint32))
+
+
+def test_reduce_scatter_flavour_through_strided_combine():
+    """The merged head slice without the write-back: dcp_unpack_combine over a
+    strided view of the partial stack (heads [h0,h1)) equals the in-place
+    merge's slice."""
+    w, inp = kimi_small(16)
+    lse = torch.from_numpy(inp["lse"]).to(DEV)
+    part = torch.from_numpy(inp["out"]).to(DEV)
+    h0, h1 = 24, 36
+    rs, g = ops.dcp_lse_combine(part[:, :, h0:h1], lse[:, :, h0:h1], is_lse_base_on_e=True)
+    scaled, ref, gr, mag = orc.inplace(inp["out"], inp["lse"], "f32", False, h0=h0, h1=h1)
+    check_out(rs.cpu().numpy(), ref, mag, "f32")
+    check_lse(g.cpu().numpy(), gr)
+
+
+def test_inplace_full_size_sampled():
+    """8 x [16384, 96, 512] fp32 partials (24 GiB) merged in place in one call,
+    in the launch configuration the benchmark times; 3000 sampled (t, h) rows
+    are checked (scaled partials of all ranks, merged row, G)."""
+    w = synth.WORKLOADS["kimi"]
+    say("inplace full size", w.describe())
+    part = synth.kimi_partial_device(w, DEV)
+    lse_np = synth.kimi_lse(w)
+    lse = torch.from_numpy(lse_np).to(DEV)
+    rng = np.random.default_rng(99)
+    T, H = w.B, w.H
+    ts = rng.integers(0, T, size=3000)
+    hs = rng.integers(0, H, size=3000)
+    # make sure sampled rows include special LSE entries
+    sp = np.argwhere(~np.isfinite(lse_np))[:200]
+    ts = np.concatenate([ts, sp[:, 1]]); hs = np.concatenate([hs, sp[:, 2]])
+    ti, hi = torch.from_numpy(ts).to(DEV), torch.from_numpy(hs).to(DEV)
+    before = part[:, ti, hi].cpu().numpy()             # [N, S, D] inputs of the sampled rows
+    out, g = ops.cp_lse_combine_inplace(part, lse, return_lse=True)
+    torch.cuda.synchronize()
+    after = part[:, ti, hi].cpu().numpy()
+    got_out = out[ti, hi].cpu().numpy()
+    got_g = g[ti, hi].cpu().numpy()
+    S = len(ts)
+    scaled, ref, gr, mag = orc.inplace(before.reshape(w.N, S, 1, w.D), lse_np[:, ts, hs].reshape(w.N, S, 1), "f32", False)
+    check_scaled(after, scaled.reshape(w.N, S, w.D), "f32")
+    check_out(got_out, ref.reshape(S, w.D), mag.reshape(S, w.D), "f32")
+    check_lse(got_g, gr.reshape(S))
+    del part, out
+    torch.cuda.empty_cache()
