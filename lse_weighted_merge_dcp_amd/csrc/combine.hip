@@ -226,6 +226,88 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
     }
 }
 
+
+// Row-per-wave variant (LPR = 64, 16-byte vectors, fixed N <= 16): the row
+// is wave-uniform, so the N peer rows are read with raw buffer loads that
+// share one VGPR lane offset (the per-peer offsets live in scalar registers)
+// and the weights are moved to scalar registers.  That keeps the kernel at
+// about 64 VGPRs, i.e. 8 waves per SIMD.  Requires every peer offset
+// (N-1) * r_N + row bytes to fit in 31 bits (checked by the launcher).
+template <typename DT, int NT>
+__global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
+    using C = Cvt<DT, 16>;
+    constexpr int EPV = C::n;
+    const uint32_t blk = xcd_block();
+    const uint32_t wave = wave_id();
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t j = lane & 15u;
+    const uint32_t row = blk * 4u + wave;
+    if (row >= k.rows) return;  // wave-uniform
+    const bool base2 = k.base2 != 0;
+    const uint32_t bb = fdiv(row, k.f_Hpr);
+    const uint32_t hl = row - bb * k.Hpr;
+    const uint32_t r = fdiv(bb, k.f_B);
+    const uint32_t b = bb - r * k.B;
+    const char* rbase = k.recv + r * k.r_R + b * k.r_B + hl * k.r_H;
+    const char* lbase = k.rlse + r * k.rl_R + b * k.rl_B + hl * k.rl_H;
+    char* obase = k.out + r * k.o_R + b * k.o_B + hl * k.o_H;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)rbase, (short)0, (int)0xFFFFFFFF, (int)0x00020000);
+
+    float lj = -INFINITY;
+    if (j < (uint32_t)NT) lj = load_f32(lbase + (int64_t)j * k.rl_N);
+    LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj), base2);
+    float w = 0.0f;
+    if (st.live) {
+        const float e = (j < (uint32_t)NT) ? exp_base(lj - st.m, base2) : 0.0f;
+        const float s = row_sum(e);
+        st.G = st.m + log_base(s, base2);
+        w = e / s;
+    }
+    float wi[NT];
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((wi[I] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, row_bcast<I>(w))))),
+         ...);
+    }(std::make_integer_sequence<int, NT>{});
+
+    for (uint32_t step = 0; step < k.steps; ++step) {
+        const uint32_t c = step * 64u + lane;
+        if (c < k.chunks) {
+            const int voff = (int)(c * 16u);
+            Vec<16> x[NT];
+#pragma unroll
+            for (int i = 0; i < NT; ++i) x[i] = buffer_vload16(rsrc, voff, (int)((uint32_t)i * (uint32_t)k.r_N));
+            float acc[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                float f[EPV];
+                C::unpack(x[i], f);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], f[e], acc[e]);
+            }
+            bool bad = false;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
+            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    float f[EPV];
+                    C::unpack(buffer_vload16(rsrc, voff, (int)((uint32_t)i * (uint32_t)k.r_N)), f);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
+                }
+            }
+            vstore<16>(obase + voff, C::pack(acc));
+        }
+    }
+    if (k.olse != nullptr && lane == 0)
+        *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
+}
+
 template <typename DT, int V, int LPR, int NT>
 hipError_t run(const CombineArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR);
@@ -262,7 +344,17 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             k.f_B = make_fastdiv(k.B);
             k.base2 = a.base2 ? 1 : 0;
             const int64_t blocks = (rows + RPB - 1) / RPB;
-            hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+            const bool wave_path = V == 16 && LPR == 64 && NT > 0 &&
+                                   (a.N - 1) * a.r_N + a.D * DT::esize < (int64_t(1) << 31);
+            if constexpr (V == 16 && LPR == 64 && NT > 0) {
+                if (wave_path) {
+                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                } else {
+                    hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                }
+            } else {
+                hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+            }
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

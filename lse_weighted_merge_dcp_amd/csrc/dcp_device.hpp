@@ -56,6 +56,16 @@ template <> __device__ __forceinline__ void vstore<2>(char* p, const Vec<2>& v) 
     *reinterpret_cast<uint16_t*>(p) = v.h;
 }
 
+// 16 bytes from a raw buffer: base in the descriptor, per-lane byte offset
+// voff and a wave-uniform byte offset soff (both below 2^31).
+__device__ __forceinline__ Vec<16> buffer_vload16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+    Vec<16> v;
+    v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
+    return v;
+}
+
 __device__ __forceinline__ uint32_t load_word(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ void store_word(char* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }
 __device__ __forceinline__ float load_f32(const char* p) { return *reinterpret_cast<const float*>(p); }

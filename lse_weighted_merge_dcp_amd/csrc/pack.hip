@@ -7,9 +7,12 @@
 // LPR consecutive chunks of one row per step; rows longer than LPR*V take
 // several steps ("virtual rows" = rows x steps).  A 256-thread block runs
 // 4 waves x (64/LPR) row groups x U virtual rows, all U loads in flight
-// before the U stores.  With LPR = 64 a virtual row is wave-uniform, so its
-// index arithmetic runs on the scalar unit.  Each payload byte is read once
-// and written once; the LSE word rides along with chunk 0 of step 0.
+// before the U stores, and exits (a one-shot grid: on gfx9 a wave that loops
+// waits for its earlier stores before reusing registers, which measured
+// slower).  With LPR = 64 a virtual row is wave-uniform, so its index
+// arithmetic runs on the scalar unit.  Each payload byte is read once and
+// written once; the LSE words of a wave's rows move in one extra load and
+// store after the payload.
 #include "dcp_device.hpp"
 #include "dcp_launch.hpp"
 
@@ -36,8 +39,11 @@ constexpr int kPackU = 4;
 
 template <int V, int LPR, int U>
 __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
+    static_assert(U <= LPR, "one LSE lane per row of the wave");
     constexpr uint32_t RPW = 64 / LPR;
-    const uint32_t blk = xcd_block();
+    // Plain block order: measured faster than an XCD-contiguous renumbering
+    // for this pure stream (reads and writes each touch a line once).
+    const uint32_t blk = blockIdx.x;
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t li = lane % LPR;
@@ -45,13 +51,15 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
 
     Vec<V> v[U];
     char* dp[U];
-    uint32_t lw[U];
-    char* dlp[U];
-    bool pl[U], ll[U];
+    bool pl[U];
+    // The LSE words of the U rows go through lanes li = 0..U-1 of each row
+    // group: one load and one store instruction per wave, issued after the
+    // payload so they never delay it.
+    const char* lsrc = nullptr;
+    char* ldst = nullptr;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         pl[u] = false;
-        ll[u] = false;
         const uint32_t vrow = (blk * (uint32_t)U + (uint32_t)u) * (4u * RPW) + wave * RPW + g;
         if (vrow < k.vrows) {
             const uint32_t row = (k.steps == 1) ? vrow : fdiv(vrow, k.f_steps);
@@ -64,23 +72,22 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
             const uint32_t hl = h - p * k.Hpr;
             const uint32_t c = step * LPR + li;
             if (k.dst != nullptr && c < k.chunks) {
-                const char* sp = k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V;
-                v[u] = vload<V>(sp);
+                v[u] = vload<V>(k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V);
                 dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + hl * k.d_H + (int64_t)c * V;
                 pl[u] = true;
             }
-            if (k.dst_lse != nullptr && step == 0 && li == 0) {
-                lw[u] = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H);
-                dlp[u] = k.dst_lse + r * k.dl_R + p * k.dl_N + b * k.dl_B + hl * k.dl_H;
-                ll[u] = true;
+            if (k.dst_lse != nullptr && step == 0 && li == (uint32_t)u) {
+                lsrc = k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H;
+                ldst = k.dst_lse + r * k.dl_R + p * k.dl_N + b * k.dl_B + hl * k.dl_H;
             }
         }
     }
+    uint32_t lw = 0;
+    if (lsrc != nullptr) lw = load_word(lsrc);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u)
         if (pl[u]) vstore<V>(dp[u], v[u]);
-        if (ll[u]) store_word(dlp[u], lw[u]);
-    }
+    if (ldst != nullptr) store_word(ldst, lw);
 }
 
 template <int V, int LPR>

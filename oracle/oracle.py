@@ -40,7 +40,7 @@ def compile_source(src: str, out: str) -> str:
     """gcc -O2 -fopenmp of an oracle C source into a shared library."""
     tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call(
-        ["gcc", "-O2", "-fopenmp", "-march=native", "-fno-fast-math", "-shared", "-fPIC",
+        ["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-shared", "-fPIC",
          "-Wall", "-Wextra", src, "-o", tmp, "-lm"])
     os.replace(tmp, out)
     return out
