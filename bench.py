@@ -22,8 +22,8 @@ bounded sample.
 Other modes:
   --counter-run       run a 1 GiB plain copy and a few launches of each kernel
                       (the command to put under rocprofv3 --pmc)
-  --summarize-counters DIR   turn rocprofv3 counter CSVs in DIR into
-                      profiles/counters_<workload>.json (+ a .md summary)
+  --summarize-counters DIR[,DIR]   turn the rocprofv3 counter CSVs found in
+                      the directories into profiles/counters_<workload>.json
 """
 from __future__ import annotations
 
@@ -400,15 +400,16 @@ def main():
 
 
 def counter_run(wl):
-    """For rocprofv3 --pmc: a 1 GiB plain copy (the scale reference), then
-    three launches of each kernel of the workload."""
+    """For rocprofv3 --pmc: a plain elementwise pass over 1 GiB (the scale
+    reference: 1 GiB read, 1 GiB written), then three launches of each kernel
+    of the workload."""
     import torch
 
-    n = 1 << 29
-    a = torch.ones(n, dtype=torch.bfloat16, device=wl.dev)
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device=wl.dev)
     b = torch.empty_like(a)
     for _ in range(3):
-        b.copy_(a)
+        torch.neg(a, out=b)   # one elementwise dispatch: reads 1 GiB, writes 1 GiB
     torch.cuda.synchronize()
     del a, b
     for name, nbytes, launches in wl.kernels():
@@ -436,7 +437,10 @@ def summarize_counters(directory, workload):
     import csv
 
     rows = []
-    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+    paths = []
+    for d in directory.split(","):
+        paths += glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    for path in paths:
         with open(path) as f:
             rows += list(csv.DictReader(f))
     by = {}
@@ -450,9 +454,9 @@ def summarize_counters(directory, workload):
         vals = [v for (k, c), vs in by.items() if pattern in k and c == cn for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    copy_bytes = (1 << 29) * 2
-    f_copy = pick("elementwise_kernel", "FETCH_SIZE")
-    w_copy = pick("elementwise_kernel", "WRITE_SIZE")
+    copy_bytes = 1 << 30      # torch.neg over 2^28 fp32: 1 GiB read, 1 GiB written
+    f_copy = pick("neg_kernel", "FETCH_SIZE")
+    w_copy = pick("neg_kernel", "WRITE_SIZE")
     if f_copy is None or w_copy is None:
         raise SystemExit("no copy-reference counters found in %s" % directory)
     fs = copy_bytes / f_copy       # bytes per counter unit, from a copy of known size
@@ -460,7 +464,7 @@ def summarize_counters(directory, workload):
     out = {"kernel_source": kernel_source_hash(), "workload": workload,
            "copy_reference": {"bytes": copy_bytes, "FETCH_SIZE": f_copy, "WRITE_SIZE": w_copy,
                               "fetch_scale": fs, "write_scale": ws}, "kernels": {}}
-    for kname, pat in (("pack", "pack_kernel"), ("combine", "combine_kernel"), ("inplace", "inplace_kernel")):
+    for kname, pat in (("pack", "pack_kernel"), ("combine", "combine_"), ("inplace", "inplace_kernel")):
         f = pick(pat, "FETCH_SIZE")
         wv = pick(pat, "WRITE_SIZE")
         if f is None or wv is None:

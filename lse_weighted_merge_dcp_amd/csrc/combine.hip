@@ -5,8 +5,10 @@
 // Per output row (r, b, hl):  G = log_beta sum_i beta^l_i,
 // w_i = nan_to_num(beta^(l_i - G)),  out = sum_i w_i * nan_to_num(o_i).
 //
-// Work mapping.  One row group of LPR lanes (16, 32 or 64) owns one output
-// row.  Inside it, every 16-lane DPP row redundantly derives G and the
+// Work mapping.  One row group of LPR lanes (16, 32 or 64) owns one segment
+// (LPR x vector bytes) of one output row; rows longer than that are split
+// over several groups, each redoing the (tiny) LSE reduction, so no wave
+// ever waits on its own stores before loading again.  Inside a group, every 16-lane DPP row redundantly derives G and the
 // weights: lane j loads l_j, the maximum, the special-value flags and the
 // sum of beta^(l_j - m) are reduced with row_ror DPP steps, and each lane's
 // w_j = beta^(l_j - m) / sum is broadcast to the row with row_newbcast.  The
@@ -38,11 +40,11 @@ struct CombK {
     int64_t rl_R, rl_N, rl_B, rl_H;
     int64_t o_R, o_B, o_H;
     int64_t ol_R, ol_B, ol_H;
-    uint32_t rows;    // R * B * Hpr in this launch
+    uint32_t rows;    // R * B * Hpr * steps tasks in this launch
     uint32_t N, B, Hpr;
     uint32_t chunks;  // D * esize / V
-    uint32_t steps;   // ceil(chunks / LPR)
-    FastDiv f_Hpr, f_B;
+    uint32_t steps;   // segments per row: ceil(chunks / LPR)
+    FastDiv f_Hpr, f_B, f_steps;
     int base2;
 };
 
@@ -91,10 +93,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
     const uint32_t li = lane % LPR;
     const uint32_t g = lane / LPR;
     const uint32_t j = lane & 15u;
-    const uint32_t row = (blk * 4u + wave) * RPW + g;
-    if (row >= k.rows) return;  // whole row groups (and so whole DPP rows) leave together
+    const uint32_t task = (blk * 4u + wave) * RPW + g;
+    if (task >= k.rows) return;  // whole row groups (and so whole DPP rows) leave together
     const bool base2 = k.base2 != 0;
 
+    const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
+    const uint32_t seg = task - row * k.steps;
     const uint32_t bb = fdiv(row, k.f_Hpr);
     const uint32_t hl = row - bb * k.Hpr;
     const uint32_t r = fdiv(bb, k.f_B);
@@ -119,8 +123,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
         [&]<int... I>(std::integer_sequence<int, I...>) { ((wi[I] = row_bcast<I>(w)), ...); }
         (std::make_integer_sequence<int, NT>{});
 
-        for (uint32_t step = 0; step < k.steps; ++step) {
-            const uint32_t c = step * LPR + li;
+        {
+            const uint32_t c = seg * LPR + li;
             if (c < k.chunks) {
                 const int64_t coff = (int64_t)c * V;
                 Vec<V> x[NT];
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
                 vstore<V>(obase + coff, C::pack(acc));
             }
         }
-        if (k.olse != nullptr && li == 0)
+        if (k.olse != nullptr && li == 0 && seg == 0)
             *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
     } else {
         // ---- any N: lane j of every DPP row covers peers j, j+16, ... -----
@@ -174,8 +178,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
             st.G = st.m + log_base(s, base2);
         }
         constexpr int PB = 8;  // peers in flight per lane
-        for (uint32_t step = 0; step < k.steps; ++step) {
-            const uint32_t c = step * LPR + li;
+        {
+            const uint32_t c = seg * LPR + li;
             if (c < k.chunks) {
                 const int64_t coff = (int64_t)c * V;
                 float acc[EPV];
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
                 vstore<V>(obase + coff, C::pack(acc));
             }
         }
-        if (k.olse != nullptr && li == 0)
+        if (k.olse != nullptr && li == 0 && seg == 0)
             *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
     }
 }
@@ -241,9 +245,11 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t j = lane & 15u;
-    const uint32_t row = blk * 4u + wave;
-    if (row >= k.rows) return;  // wave-uniform
+    const uint32_t task = blk * 4u + wave;
+    if (task >= k.rows) return;  // wave-uniform
     const bool base2 = k.base2 != 0;
+    const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
+    const uint32_t seg = task - row * k.steps;
     const uint32_t bb = fdiv(row, k.f_Hpr);
     const uint32_t hl = row - bb * k.Hpr;
     const uint32_t r = fdiv(bb, k.f_B);
@@ -270,8 +276,8 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
          ...);
     }(std::make_integer_sequence<int, NT>{});
 
-    for (uint32_t step = 0; step < k.steps; ++step) {
-        const uint32_t c = step * 64u + lane;
+    {
+        const uint32_t c = seg * 64u + lane;
         if (c < k.chunks) {
             const int voff = (int)(c * 16u);
             Vec<16> x[NT];
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
             vstore<16>(obase + voff, C::pack(acc));
         }
     }
-    if (k.olse != nullptr && lane == 0)
+    if (k.olse != nullptr && lane == 0 && seg == 0)
         *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
 }
 
@@ -313,12 +319,12 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR);
     const int64_t chunks = a.D * DT::esize / V;
     const int64_t steps = (chunks + LPR - 1) / LPR;
-    const int64_t per_r = a.B * a.Hpr;
+    const int64_t per_r = a.B * a.Hpr * steps;
     int64_t r_chunk = per_r > 0 ? kMaxRowsPerLaunch / per_r : a.R;
     int64_t b_chunk = a.B;
     if (r_chunk < 1) {
         r_chunk = 1;
-        b_chunk = kMaxRowsPerLaunch / a.Hpr;
+        b_chunk = kMaxRowsPerLaunch / (a.Hpr * steps);
     }
     for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
         const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;
@@ -333,7 +339,7 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             k.rl_R = a.rl_R; k.rl_N = a.rl_N; k.rl_B = a.rl_B; k.rl_H = a.rl_H;
             k.o_R = a.o_R; k.o_B = a.o_B; k.o_H = a.o_H;
             k.ol_R = a.ol_R; k.ol_B = a.ol_B; k.ol_H = a.ol_H;
-            const int64_t rows = nr * nb * a.Hpr;
+            const int64_t rows = nr * nb * a.Hpr * steps;   // (r, b, hl, segment) tasks
             k.rows = (uint32_t)rows;
             k.N = (uint32_t)a.N;
             k.B = (uint32_t)nb;
@@ -342,6 +348,7 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             k.steps = (uint32_t)steps;
             k.f_Hpr = make_fastdiv(k.Hpr);
             k.f_B = make_fastdiv(k.B);
+            k.f_steps = make_fastdiv(k.steps);
             k.base2 = a.base2 ? 1 : 0;
             const int64_t blocks = (rows + RPB - 1) / RPB;
             const bool wave_path = V == 16 && LPR == 64 && NT > 0 &&

@@ -66,6 +66,26 @@ __device__ __forceinline__ Vec<16> buffer_vload16(__amdgpu_buffer_rsrc_t rsrc, i
     return v;
 }
 
+// Streaming variants: the nontemporal hint tells the caches the line is used
+// once (a partial read once, a write-back nobody reads again).
+__device__ __forceinline__ Vec<16> vload16_stream(const char* p) {
+    const u32x4_a4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
+    Vec<16> v;
+    v.w[0] = x.x; v.w[1] = x.y; v.w[2] = x.z; v.w[3] = x.w;
+    return v;
+}
+__device__ __forceinline__ void vstore16_stream(char* p, const Vec<16>& v) {
+    u32x4_a4 x;
+    x.x = v.w[0]; x.y = v.w[1]; x.z = v.w[2]; x.w = v.w[3];
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_a4*>(p));
+}
+template <int V> __device__ __forceinline__ Vec<V> vload_stream(const char* p) {
+    if constexpr (V == 16) return vload16_stream(p); else return vload<V>(p);
+}
+template <int V> __device__ __forceinline__ void vstore_stream(char* p, const Vec<V>& v) {
+    if constexpr (V == 16) vstore16_stream(p, v); else vstore<V>(p, v);
+}
+
 __device__ __forceinline__ uint32_t load_word(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ void store_word(char* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }
 __device__ __forceinline__ float load_f32(const char* p) { return *reinterpret_cast<const float*>(p); }

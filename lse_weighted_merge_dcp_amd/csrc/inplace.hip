@@ -5,14 +5,22 @@
 // does the scaling with PyTorch ops, an all-reduce and a slice copy; here one
 // pass reads each partial row once, writes it back once, and writes the slice.
 //
-// Work mapping as in combine.hip: one row group of LPR lanes per (t, h) row;
-// each 16-lane DPP row derives G and the weights of all N ranks from the
-// LSE stack with DPP reductions; the payload streams in 16-byte vectors with
-// all P held partials in flight per lane.  The fast path (P == N in
+// Work mapping: one row group of LPR lanes per (t, h, segment) task, where a
+// segment is the LPR x 16 bytes of the row one step of the group covers (a
+// 2 KB fp32 row of D = 512 is two segments, two waves).  Each wave then
+// issues its loads once and never waits on its own stores (gfx9 counts
+// loads and stores in one in-order counter, so a second step would).  Each
+// 16-lane DPP row derives G and the weights of all N ranks from the LSE
+// stack with DPP reductions (redundantly per segment; it is a few words);
+// the payload streams in 16-byte vectors with all P held partials in flight
+// per lane, read and written back with the nontemporal hint (each partial
+// line is touched once and is dead afterwards).  The fast path (P == N in
 // {2,4,8,16}, rank0 == 0: every rank stacked on this GPU) broadcasts weights
-// with row_newbcast; otherwise each lane recomputes the weight of the rank it
-// streams.  Guards as in combine.hip: a finite row sum proves every scaled
-// term finite; otherwise the terms are re-formed from guarded values.
+// with row_newbcast; otherwise each lane recomputes the weight of the rank
+// it streams and applies the guards directly.  Guards in the fast path as in
+// combine.hip: a finite row sum proves every scaled term finite; otherwise
+// the terms are re-formed from guarded values.  Blocks run in plain order
+// (measured faster than an XCD-contiguous order for these aligned rows).
 #include <math.h>
 
 #include "dcp_device.hpp"
@@ -32,8 +40,8 @@ struct InplK {
     int64_t ol_T, ol_H;
     uint32_t rows;  // T * H in this launch
     uint32_t N, P, rank0, H, h0, h1;
-    uint32_t chunks, steps;
-    FastDiv f_H;
+    uint32_t chunks, steps;  // steps = segments per row
+    FastDiv f_H, f_steps;
     int base2;
 };
 
@@ -46,16 +54,18 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
     using C = Cvt<DT, V>;
     constexpr int EPV = C::n;
     constexpr uint32_t RPW = 64 / LPR;
-    const uint32_t blk = xcd_block();
+    const uint32_t blk = blockIdx.x;
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t li = lane % LPR;
     const uint32_t g = lane / LPR;
     const uint32_t j = lane & 15u;
-    const uint32_t row = (blk * 4u + wave) * RPW + g;
-    if (row >= k.rows) return;  // whole row groups leave together
+    const uint32_t task = (blk * 4u + wave) * RPW + g;
+    if (task >= k.rows) return;  // whole row groups leave together
     const bool base2 = k.base2 != 0;
 
+    const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
+    const uint32_t seg = task - row * k.steps;
     const uint32_t t = fdiv(row, k.f_H);
     const uint32_t h = row - t * k.H;
     char* pbase = k.part + t * k.p_T + h * k.p_H;
@@ -108,13 +118,13 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
         float wi[NT];
         [&]<int... I>(std::integer_sequence<int, I...>) { ((wi[I] = row_bcast<I>(w)), ...); }
         (std::make_integer_sequence<int, NT>{});
-        for (uint32_t step = 0; step < k.steps; ++step) {
-            const uint32_t c = step * LPR + li;
+        {
+            const uint32_t c = seg * LPR + li;
             if (c < k.chunks) {
                 const int64_t coff = (int64_t)c * V;
                 Vec<V> x[NT];
 #pragma unroll
-                for (int i = 0; i < NT; ++i) x[i] = vload<V>(pbase + i * k.p_N + coff);
+                for (int i = 0; i < NT; ++i) x[i] = vload_stream<V>(pbase + i * k.p_N + coff);
                 float sc[NT][EPV];
                 float acc[EPV];
 #pragma unroll
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < NT; ++i) vstore<V>(pbase + i * k.p_N + coff, C::pack(sc[i]));
+                for (int i = 0; i < NT; ++i) vstore_stream<V>(pbase + i * k.p_N + coff, C::pack(sc[i]));
                 if (obase != nullptr) vstore<V>(obase + coff, C::pack(acc));
             }
         }
@@ -154,8 +164,8 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
         // (not the stacked-ranks hot path: the guards are applied directly)
         const int P = (int)k.P;
         constexpr int PB = 8;
-        for (uint32_t step = 0; step < k.steps; ++step) {
-            const uint32_t c = step * LPR + li;
+        {
+            const uint32_t c = seg * LPR + li;
             if (c < k.chunks) {
                 const int64_t coff = (int64_t)c * V;
                 float acc[EPV];
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
                     for (int q = 0; q < PB; ++q) {
                         wv[q] = 0.0f;
                         if (j0 + q < P) {
-                            x[q] = vload<V>(pbase + (j0 + q) * k.p_N + coff);
+                            x[q] = vload_stream<V>(pbase + (j0 + q) * k.p_N + coff);
                             if (live)
                                 wv[q] = exp_base(load_f32(lbase + (int64_t)(k.rank0 + j0 + q) * k.l_N) - m, base2) / s;
                         }
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
                                 f[e] = guard_f(f[e]) * wv[q];
                                 acc[e] += f[e];
                             }
-                            vstore<V>(pbase + (j0 + q) * k.p_N + coff, C::pack(f));
+                            vstore_stream<V>(pbase + (j0 + q) * k.p_N + coff, C::pack(f));
                         }
                     }
                 }
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
             }
         }
     }
-    if (k.olse != nullptr && in_slice && li == 0)
+    if (k.olse != nullptr && in_slice && li == 0 && seg == 0)
         *reinterpret_cast<float*>(k.olse + t * k.ol_T + (h - k.h0) * k.ol_H) = G;
 }
 
@@ -200,7 +210,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR);
     const int64_t chunks = a.D * DT::esize / V;
     const int64_t steps = (chunks + LPR - 1) / LPR;
-    const int64_t t_chunk = kMaxRowsPerLaunch / a.H;
+    const int64_t t_chunk = kMaxRowsPerLaunch / (a.H * steps);
     for (int64_t t0 = 0; t0 < a.T; t0 += t_chunk) {
         const int64_t nt = t0 + t_chunk <= a.T ? t_chunk : a.T - t0;
         InplK k;
@@ -212,7 +222,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
         k.l_N = a.l_N; k.l_T = a.l_T; k.l_H = a.l_H;
         k.o_T = a.o_T; k.o_H = a.o_H;
         k.ol_T = a.ol_T; k.ol_H = a.ol_H;
-        const int64_t rows = nt * a.H;
+        const int64_t rows = nt * a.H * steps;   // (t, h, segment) tasks
         k.rows = (uint32_t)rows;
         k.N = (uint32_t)a.N;
         k.P = (uint32_t)a.P;
@@ -223,6 +233,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
         k.chunks = (uint32_t)chunks;
         k.steps = (uint32_t)steps;
         k.f_H = make_fastdiv(k.H);
+        k.f_steps = make_fastdiv(k.steps);
         k.base2 = a.base2 ? 1 : 0;
         const int64_t blocks = (rows + RPB - 1) / RPB;
         hipLaunchKernelGGL((inplace_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
