@@ -90,6 +90,151 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
     if (ldst != nullptr) store_word(ldst, lw);
 }
 
+
+// ---------------------------------------------------------------------------
+// Interleaved fast path.  In a peer-outer interleaved send buffer the Hpr rows
+// of one (rank r, peer p, token b) are one contiguous block of Hpr * W bytes,
+// W = row_bytes + 4: each payload row followed by its LSE word.  When that
+// block is 16-byte aligned, the pack writes it as a flat stream of aligned
+// 16-byte chunks (full-line stores, the LSE words inside them) instead of
+// rows that start 4 bytes apart.  The source side of the block is the Hpr
+// payload rows of heads p*Hpr.. (contiguous in a [B,H,D] partial), so the
+// payload dword j of the block comes from source dword j - k, where k is the
+// row it sits in; a chunk that holds the LSE word of row k takes three
+// payload dwords from source dwords base-1..base+2 and the LSE in between.
+// A wave-step covers 64 chunks (256 dwords); with W >= 1024 bytes it holds at
+// most one LSE word, at a wave-uniform position, so the LSE arrives through a
+// scalar load.
+// ---------------------------------------------------------------------------
+struct StreamK {
+    const char* src;
+    const char* src_lse;
+    char* dst;
+    int64_t s_R, s_B;          // source bytes per rank / token; head rows are row_bytes apart
+    int64_t sl_R, sl_B, sl_H;  // source LSE bytes
+    int64_t d_R, d_N, d_B;     // destination block bytes
+    uint32_t nsteps;           // R * B * N * S wave-steps in this launch
+    uint32_t S;                // wave-steps per block = ceil(Q / 64)
+    uint32_t Q;                // 16-byte chunks per block = Hpr * W / 16
+    uint32_t Wd;               // dwords per row incl. the LSE word = W / 4 (>= 256)
+    uint32_t Hpr, N, B;
+    FastDiv f_S, f_N, f_B, f_Wd;
+};
+
+constexpr int kStreamU = 2;
+
+template <int U>
+__global__ __launch_bounds__(256) void pack_stream_kernel(const StreamK k) {
+    const uint32_t wave = wave_id();
+    const uint32_t lane = threadIdx.x & 63u;
+    Vec<16> v[U];
+    char* dp[U];
+    bool on[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        on[u] = false;
+        const uint32_t ws = (blockIdx.x * (uint32_t)U + (uint32_t)u) * 4u + wave;  // wave-uniform
+        if (ws < k.nsteps) {
+            const uint32_t blk = fdiv(ws, k.f_S);       // blocks ordered (r, b, p): sequential source reads
+            const uint32_t s = ws - blk * k.S;
+            const uint32_t rb = fdiv(blk, k.f_N);
+            const uint32_t p = blk - rb * k.N;
+            const uint32_t r = fdiv(rb, k.f_B);
+            const uint32_t b = rb - r * k.B;
+            // the LSE word in dwords [256 s, 256 s + 256) of the block, if any:
+            // the first LSE at or after dword d0 belongs to row d0 / Wd
+            const uint32_t d0 = s * 256u;
+            const uint32_t kl = fdiv(d0, k.f_Wd);
+            const uint32_t jl = kl * k.Wd + k.Wd - 1u;
+            uint32_t lval = 0;
+            if (kl < k.Hpr && jl >= d0 && jl < d0 + 256u)
+                lval = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + kl) * k.sl_H);
+            const uint32_t q = s * 64u + lane;
+            if (q < k.Q) {
+                const uint32_t j0 = q * 4u;                   // first dword of the chunk
+                const uint32_t row = fdiv(j0, k.f_Wd);
+                const uint32_t t = k.Wd - 1u - (j0 - row * k.Wd);   // LSE position in the chunk if < 4
+                const bool has_lse = t < 4u;
+                const uint32_t base = j0 - row;               // source dword of the chunk's first payload dword
+                const char* sblk = k.src + r * k.s_R + b * k.s_B + (int64_t)(p * k.Hpr) * ((int64_t)(k.Wd - 1u) * 4);
+                Vec<16> x = vload<16>(sblk + (int64_t)(has_lse ? base - 1u : base) * 4);
+                if (has_lse) {
+                    uint32_t o[4];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        o[d] = (uint32_t)d < t ? x.w[d + 1] : ((uint32_t)d == t ? lval : x.w[d]);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) x.w[d] = o[d];
+                }
+                v[u] = x;
+                dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + (int64_t)q * 16;
+                on[u] = true;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (on[u]) vstore<16>(dp[u], v[u]);
+}
+
+// True when dst/dst_lse form a peer-outer interleaved buffer whose blocks the
+// stream kernel can write: LSE word right after each payload row, rows
+// contiguous, 16-byte aligned blocks, rows of at least 1 KB, and the source
+// head rows contiguous and dword aligned.
+bool stream_layout(const PackArgs& a) {
+    if (a.dst == nullptr || a.dst_lse == nullptr || a.Hpr < 1) return false;
+    const int64_t W = a.row_bytes + 4;
+    if (a.row_bytes % 4 != 0 || W / 4 < 256) return false;
+    if (a.dst_lse != a.dst + a.row_bytes) return false;
+    if (a.d_H != W || a.dl_H != W || a.dl_R != a.d_R || a.dl_N != a.d_N || a.dl_B != a.d_B) return false;
+    if ((uintptr_t)a.dst % 16 || a.d_R % 16 || a.d_N % 16 || a.d_B % 16 || (a.Hpr * W) % 16) return false;
+    if (a.s_H != a.row_bytes || (uintptr_t)a.src % 4 || a.s_R % 4 || a.s_B % 4) return false;
+    return true;
+}
+
+hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
+    const int64_t N = a.H / a.Hpr;
+    const int64_t W = a.row_bytes + 4;
+    const int64_t Q = a.Hpr * W / 16;
+    const int64_t S = (Q + 63) / 64;
+    const int64_t per_r = a.B * N * S;
+    int64_t r_chunk = kMaxRowsPerLaunch / per_r;
+    int64_t b_chunk = a.B;
+    if (r_chunk < 1) {
+        r_chunk = 1;
+        b_chunk = kMaxRowsPerLaunch / (N * S);
+    }
+    for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
+        const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;
+        for (int64_t b0 = 0; b0 < a.B; b0 += b_chunk) {
+            const int64_t nb = b0 + b_chunk <= a.B ? b_chunk : a.B - b0;
+            StreamK k;
+            k.src = a.src + r0 * a.s_R + b0 * a.s_B;
+            k.src_lse = a.src_lse + r0 * a.sl_R + b0 * a.sl_B;
+            k.dst = a.dst + r0 * a.d_R + b0 * a.d_B;
+            k.s_R = a.s_R; k.s_B = a.s_B;
+            k.sl_R = a.sl_R; k.sl_B = a.sl_B; k.sl_H = a.sl_H;
+            k.d_R = a.d_R; k.d_N = a.d_N; k.d_B = a.d_B;
+            k.Q = (uint32_t)Q;
+            k.S = (uint32_t)S;
+            k.nsteps = (uint32_t)(nr * nb * N * S);
+            k.Wd = (uint32_t)(W / 4);
+            k.Hpr = (uint32_t)a.Hpr;
+            k.N = (uint32_t)N;
+            k.B = (uint32_t)nb;
+            k.f_S = make_fastdiv(k.S);
+            k.f_N = make_fastdiv(k.N);
+            k.f_B = make_fastdiv(k.B);
+            k.f_Wd = make_fastdiv(k.Wd);
+            const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
+            hipLaunchKernelGGL((pack_stream_kernel<kStreamU>), dim3(blocks), dim3(256), 0, stream, k);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
 template <int V, int LPR>
 hipError_t run(const PackArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR) * kPackU;
@@ -161,6 +306,7 @@ int pick_vec_bytes(int64_t row_bytes, int esize, const int64_t* addrs, int count
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
     if (a.R == 0 || a.B == 0) return hipSuccess;
+    if (stream_layout(a)) return run_stream(a, stream);
     int V = 4;
     if (a.dst != nullptr) {
         const int64_t addrs[] = {(int64_t)(uintptr_t)a.src, a.s_R, a.s_B, a.s_H,

@@ -72,6 +72,43 @@ def test_pack_interleaved_workloads(key, B):
     assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
 
 
+STREAM_SHAPES = [
+    ("bf16", 8, 5, 16, 512),    # the decode shape, ragged batch
+    ("bf16", 4, 3, 4, 512),     # small peer blocks (Hpr * W = 4112 B)
+    ("f32", 2, 6, 8, 256),      # fp32 rows of 1 KB (W = 1028)
+    ("f32", 4, 2, 12, 512),     # 2 KB rows: several LSE-free wave-steps per row
+    ("f16", 2, 3, 8, 1024),     # 2 KB fp16 rows
+    ("bf16", 1, 4, 8, 768),     # a single peer (N = 1)
+    ("bf16", 2, 3, 3, 512),     # Hpr * W not a multiple of 16: falls back to the row kernel
+    ("bf16", 2, 3, 8, 504),     # rows under 1 KB: row kernel
+]
+
+
+@pytest.mark.parametrize("dt,N,B,Hpr,D", STREAM_SHAPES)
+def test_pack_interleaved_stream_shapes(dt, N, B, Hpr, D):
+    """Interleaved send buffers of several shapes, two simulated source ranks
+    (R = 2), checked byte for byte with guard bands."""
+    say("pack stream shapes", dt, N, B, Hpr, D)
+    R, H = 2, N * Hpr
+    esz = np.dtype(NP_DT[dt]).itemsize
+    lpd = 4 // esz
+    g = torch.Generator().manual_seed(N * 31 + D)
+    out = synth.to_storage(torch.randn(R, B, H, D, generator=g), dt)
+    lse = np.random.default_rng(D + B).normal(size=(R, B, H)).astype(np.float32)
+    lse[0, 0, :2] = [np.nan, -np.inf]
+    shape = (R, N, B, Hpr, D + lpd)
+    buf, host = guarded(int(np.prod(shape)) * esz, seed=D + N)
+    send = dev_view(buf, TORCH_DT[dt], shape)
+    pay, words = ops.interleaved_views(send, D)
+    ops.dcp_pack_a2a_send(to_dev(out, dt, DEV), torch.from_numpy(lse).to(DEV), pay, words)
+    hsend = host_view(host, NP_DT[dt], shape)
+    hpay, hwords = orc.interleaved_views_np(hsend, D, dt)
+    for r in range(R):
+        orc.pack(out[r], lse[r], hpay[r], hwords[r], N)
+    got = buf.cpu().numpy()
+    assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
+
+
 SPLIT = [("f16", 4, 256, 16, 128), ("bf16", 2, 4, 8, 128), ("bf16", 4, 1, 16, 512), ("f32", 8, 3, 2, 64)]
 
 
