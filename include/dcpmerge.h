@@ -93,15 +93,23 @@ const char* dcp_status_str(int status);
  * Bytes the map does not address are left untouched, e.g. stats slot 1
  * (the page allocates it with empty() because nothing ever reads it).
  *
+ * kv_len (nullable) holds the rank-local KV length of every (r, b) as int32.
+ * Where it is 0 the rank owns no KV for that token, and the pack sends the
+ * neutral pair instead of the partial: payload 0 and LSE -inf for all H heads,
+ * without reading src (the fixup_zero_kv_rows pass of sglang PR #33926 report,
+ * 实现拆解 item 3, fused into the pack).  Non-zero lengths change nothing.
+ *
  * Strides: src_o (so_R, so_B, so_H) elements; src_lse (sl_R, sl_B, sl_H)
  * words; dst_o (do_R, do_N, do_B, do_H) elements; dst_lse (dl_R, dl_N, dl_B,
- * dl_H) words.  Errors: DCP_ERR_NULL, _SHAPE (R, B < 0; N, H, D < 1),
- * _HEADS_NOT_DIVISIBLE, _DTYPE, _STRIDE, _ALIGN, _LAUNCH.
+ * dl_H) words; kv_len (kl_R, kl_B) int32 elements.  Errors: DCP_ERR_NULL,
+ * _SHAPE (R, B < 0; N, H, D < 1), _HEADS_NOT_DIVISIBLE, _DTYPE, _STRIDE,
+ * _ALIGN (also kv_len not 4-byte aligned), _LAUNCH.
  */
 int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
              const float* src_lse, int64_t sl_R, int64_t sl_B, int64_t sl_H,
              void* dst_o, int64_t do_R, int64_t do_N, int64_t do_B, int64_t do_H,
              float* dst_lse, int64_t dl_R, int64_t dl_N, int64_t dl_B, int64_t dl_H,
+             const int32_t* kv_len, int64_t kl_R, int64_t kl_B,
              int64_t R, int64_t N, int64_t B, int64_t H, int64_t D,
              int dtype, void* stream);
 

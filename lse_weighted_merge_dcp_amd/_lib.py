@@ -37,6 +37,7 @@ SIGNATURES = {
                   _VP, _I64, _I64, _I64,
                   _VP, _I64, _I64, _I64, _I64,
                   _VP, _I64, _I64, _I64, _I64,
+                  _VP, _I64, _I64,
                   _I64, _I64, _I64, _I64, _I64,
                   _INT, _VP], _INT),
     "dcp_unpack_combine": ([_VP, _I64, _I64, _I64, _I64,

@@ -67,6 +67,7 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
              const float* src_lse, int64_t sl_R, int64_t sl_B, int64_t sl_H,
              void* dst_o, int64_t do_R, int64_t do_N, int64_t do_B, int64_t do_H,
              float* dst_lse, int64_t dl_R, int64_t dl_N, int64_t dl_B, int64_t dl_H,
+             const int32_t* kv_len, int64_t kl_R, int64_t kl_B,
              int64_t R, int64_t N, int64_t B, int64_t H, int64_t D,
              int dtype, void* stream) {
     const int e = esize_of(dtype);
@@ -74,11 +75,12 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
     if (R < 0 || B < 0 || N < 1 || H < 1 || D < 1) return DCP_ERR_SHAPE;
     if (H % N != 0) return DCP_ERR_HEADS_NOT_DIVISIBLE;
     if (!shape_fits(H, D * e)) return DCP_ERR_SHAPE;
-    if (!nonneg({so_R, so_B, so_H, sl_R, sl_B, sl_H, do_R, do_N, do_B, do_H, dl_R, dl_N, dl_B, dl_H}))
+    if (!nonneg({so_R, so_B, so_H, sl_R, sl_B, sl_H, do_R, do_N, do_B, do_H, dl_R, dl_N, dl_B, dl_H, kl_R, kl_B}))
         return DCP_ERR_STRIDE;
     if (R == 0 || B == 0) return DCP_OK;
     if (!src_o || !src_lse || !dst_o || !dst_lse) return DCP_ERR_NULL;
-    if (!aligned(src_o, e) || !aligned(dst_o, e) || !aligned(src_lse, 4) || !aligned(dst_lse, 4))
+    if (!aligned(src_o, e) || !aligned(dst_o, e) || !aligned(src_lse, 4) || !aligned(dst_lse, 4) ||
+        (kv_len && !aligned(kv_len, 4)))
         return DCP_ERR_ALIGN;
     dcp::PackArgs a;
     a.src = (const char*)src_o;
@@ -89,6 +91,8 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
     a.sl_R = sl_R * 4; a.sl_B = sl_B * 4; a.sl_H = sl_H * 4;
     a.d_R = do_R * e; a.d_N = do_N * e; a.d_B = do_B * e; a.d_H = do_H * e;
     a.dl_R = dl_R * 4; a.dl_N = dl_N * 4; a.dl_B = dl_B * 4; a.dl_H = dl_H * 4;
+    a.kv = (const char*)kv_len;
+    a.kv_R = kl_R * 4; a.kv_B = kl_B * 4;
     a.R = R; a.B = B; a.H = H; a.Hpr = H / N;
     a.row_bytes = D * e;
     a.esize = e;

@@ -40,6 +40,11 @@ template <> __device__ __forceinline__ Vec<2> vload<2>(const char* p) {
     Vec<2> v; v.h = *reinterpret_cast<const uint16_t*>(p); return v;
 }
 
+template <int V> __device__ __forceinline__ Vec<V> vzero() {
+    Vec<V> v{};
+    return v;
+}
+
 template <int V> __device__ __forceinline__ void vstore(char* p, const Vec<V>& v);
 template <> __device__ __forceinline__ void vstore<16>(char* p, const Vec<16>& v) {
     u32x4_a4 x; x.x = v.w[0]; x.y = v.w[1]; x.z = v.w[2]; x.w = v.w[3];

@@ -14,12 +14,15 @@ enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 // for r < R, b < B, h < H with p = h / Hpr, hl = h % Hpr
 //   dst[r, p, b, hl, 0:row_bytes] = src[r, b, h, 0:row_bytes]
 //   dst_lse[r, p, b, hl]          = src_lse[r, b, h]        (if dst_lse != nullptr)
-// dst == nullptr skips the payload.
+// dst == nullptr skips the payload.  kv (nullable, int32 per (r, b)): where it
+// is 0 the row is sent as the neutral pair (payload 0, LSE -inf).
 struct PackArgs {
     const char* src;
     const char* src_lse;
     char* dst;
     char* dst_lse;
+    const char* kv = nullptr;
+    int64_t kv_R = 0, kv_B = 0;
     int64_t s_R, s_B, s_H;
     int64_t sl_R, sl_B, sl_H;
     int64_t d_R, d_N, d_B, d_H;

@@ -24,6 +24,8 @@ struct PackK {
     const char* src_lse;
     char* dst;
     char* dst_lse;
+    const char* kv;            // nullable: int32 KV length per (r, b); 0 = neutral row
+    int64_t kv_R, kv_B;
     int64_t s_R, s_B, s_H;
     int64_t sl_R, sl_B, sl_H;
     int64_t d_R, d_N, d_B, d_H;
@@ -36,6 +38,7 @@ struct PackK {
 };
 
 constexpr int kPackU = 4;
+constexpr uint32_t kNegInfBits = 0xff800000u;   // -inf as an fp32 word
 
 template <int V, int LPR, int U>
 __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
@@ -71,18 +74,19 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
             const uint32_t p = fdiv(h, k.f_Hpr);
             const uint32_t hl = h - p * k.Hpr;
             const uint32_t c = step * LPR + li;
+            const bool neutral = k.kv != nullptr && load_word(k.kv + r * k.kv_R + b * k.kv_B) == 0u;
             if (k.dst != nullptr && c < k.chunks) {
-                v[u] = vload<V>(k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V);
+                v[u] = neutral ? vzero<V>() : vload<V>(k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V);
                 dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + hl * k.d_H + (int64_t)c * V;
                 pl[u] = true;
             }
             if (k.dst_lse != nullptr && step == 0 && li == (uint32_t)u) {
-                lsrc = k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H;
+                lsrc = neutral ? nullptr : k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H;
                 ldst = k.dst_lse + r * k.dl_R + p * k.dl_N + b * k.dl_B + hl * k.dl_H;
             }
         }
     }
-    uint32_t lw = 0;
+    uint32_t lw = kNegInfBits;   // the neutral pair's LSE
     if (lsrc != nullptr) lw = load_word(lsrc);
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -110,6 +114,8 @@ struct StreamK {
     const char* src;
     const char* src_lse;
     char* dst;
+    const char* kv;            // nullable: int32 KV length per (r, b); 0 = neutral block
+    int64_t kv_R, kv_B;
     int64_t s_R, s_B;          // source bytes per rank / token; head rows are row_bytes apart
     int64_t sl_R, sl_B, sl_H;  // source LSE bytes
     int64_t d_R, d_N, d_B;     // destination block bytes
@@ -146,8 +152,10 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const StreamK k) {
             const uint32_t d0 = s * 256u;
             const uint32_t kl = fdiv(d0, k.f_Wd);
             const uint32_t jl = kl * k.Wd + k.Wd - 1u;
-            uint32_t lval = 0;
-            if (kl < k.Hpr && jl >= d0 && jl < d0 + 256u)
+            // a token this rank owns no KV for is sent as the neutral pair
+            const bool neutral = k.kv != nullptr && load_word(k.kv + r * k.kv_R + b * k.kv_B) == 0u;
+            uint32_t lval = kNegInfBits;
+            if (!neutral && kl < k.Hpr && jl >= d0 && jl < d0 + 256u)
                 lval = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + kl) * k.sl_H);
             const uint32_t q = s * 64u + lane;
             if (q < k.Q) {
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const StreamK k) {
                 const bool has_lse = t < 4u;
                 const uint32_t base = j0 - row;               // source dword of the chunk's first payload dword
                 const char* sblk = k.src + r * k.s_R + b * k.s_B + (int64_t)(p * k.Hpr) * ((int64_t)(k.Wd - 1u) * 4);
-                Vec<16> x = vload<16>(sblk + (int64_t)(has_lse ? base - 1u : base) * 4);
+                Vec<16> x = neutral ? vzero<16>() : vload<16>(sblk + (int64_t)(has_lse ? base - 1u : base) * 4);
                 if (has_lse) {
                     uint32_t o[4];
 #pragma unroll
@@ -212,6 +220,8 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.src = a.src + r0 * a.s_R + b0 * a.s_B;
             k.src_lse = a.src_lse + r0 * a.sl_R + b0 * a.sl_B;
             k.dst = a.dst + r0 * a.d_R + b0 * a.d_B;
+            k.kv = a.kv ? a.kv + r0 * a.kv_R + b0 * a.kv_B : nullptr;
+            k.kv_R = a.kv_R; k.kv_B = a.kv_B;
             k.s_R = a.s_R; k.s_B = a.s_B;
             k.sl_R = a.sl_R; k.sl_B = a.sl_B; k.sl_H = a.sl_H;
             k.d_R = a.d_R; k.d_N = a.d_N; k.d_B = a.d_B;
@@ -257,6 +267,8 @@ hipError_t run(const PackArgs& a, hipStream_t stream) {
             k.src_lse = a.src_lse ? a.src_lse + r0 * a.sl_R + b0 * a.sl_B : nullptr;
             k.dst = a.dst ? a.dst + r0 * a.d_R + b0 * a.d_B : nullptr;
             k.dst_lse = a.dst_lse ? a.dst_lse + r0 * a.dl_R + b0 * a.dl_B : nullptr;
+            k.kv = a.kv ? a.kv + r0 * a.kv_R + b0 * a.kv_B : nullptr;
+            k.kv_R = a.kv_R; k.kv_B = a.kv_B;
             k.s_R = a.s_R; k.s_B = a.s_B; k.s_H = a.s_H;
             k.sl_R = a.sl_R; k.sl_B = a.sl_B; k.sl_H = a.sl_H;
             k.d_R = a.d_R; k.d_N = a.d_N; k.d_B = a.d_B; k.d_H = a.d_H;

@@ -81,14 +81,19 @@ def interleaved_views(send: torch.Tensor, D: int) -> Tuple[torch.Tensor, torch.T
     return send[..., :D], words[..., D // lpd]
 
 
-def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor, dst_lse: torch.Tensor) -> None:
+def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor, dst_lse: torch.Tensor,
+                      kv_len: Optional[torch.Tensor] = None) -> None:
     """Scatter out [B,H,D] / lse [B,H] into dst_o [N,B,H/N,D] / dst_lse
     [N,B,H/N] (any strides): head h goes to peer h // (H/N) as local head
-    h % (H/N).  With a leading R dimension on all four, R packs run at once."""
-    _on_gpu(out, lse, dst_o, dst_lse)
+    h % (H/N).  With a leading R dimension on all four, R packs run at once.
+    kv_len ([B] or [R,B] int32, optional): tokens whose rank-local KV length
+    is 0 are sent as the neutral pair (0, -inf) instead of the partial (the
+    fixup_zero_kv_rows step of sglang PR #33926 report, 实现拆解 item 3)."""
+    _on_gpu(out, lse, dst_o, dst_lse, kv_len)
     batched = out.dim() == 4
     if not batched:
         out, lse, dst_o, dst_lse = out[None], lse[None], dst_o[None], dst_lse[None]
+        kv_len = kv_len[None] if kv_len is not None else None
     _require(out.dim() == 4 and lse.dim() == 3 and dst_o.dim() == 5 and dst_lse.dim() == 4,
              "expected out [B,H,D], lse [B,H], dst_o [N,B,Hpr,D], dst_lse [N,B,Hpr] (optionally with a leading R)")
     R, B, H, D = out.shape
@@ -103,12 +108,17 @@ def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor,
     _payload_ok(dst_o, "dst_o")
     _lse_ok(lse, "lse")
     _lse_ok(dst_lse, "dst_lse")
+    kl = (0, 0)
+    if kv_len is not None:
+        _require(kv_len.dtype == torch.int32 and tuple(kv_len.shape) == (R, B), "kv_len must be int32 [R,B] / [B]")
+        kl = kv_len.stride()
     so, sl, do, dl = out.stride(), lse.stride(), dst_o.stride(), dst_lse.stride()
     st = _lib.lib().dcp_pack(
         out.data_ptr(), so[0], so[1], so[2],
         lse.data_ptr(), sl[0], sl[1], sl[2],
         dst_o.data_ptr(), do[0], do[1], do[2], do[3],
         dst_lse.data_ptr(), dl[0], dl[1], dl[2], dl[3],
+        kv_len.data_ptr() if kv_len is not None else None, kl[0], kl[1],
         R, N, B, H, D, _dt(out), _stream(out))
     _lib.check(st, "dcp_pack")
 

@@ -32,9 +32,10 @@ class StackedInterleaved:
         self.send = torch.empty((N, N, B, H // N, D + self.lpd), dtype=dtype, device=device)
         self.payload, self.words = ops.interleaved_views(self.send, D)
 
-    def pack(self, out: torch.Tensor, lse: torch.Tensor) -> None:
-        """out [N,B,H,D], lse [N,B,H]: every rank packs its own send buffer (one launch)."""
-        ops.dcp_pack_a2a_send(out, lse, self.payload, self.words)
+    def pack(self, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+        """out [N,B,H,D], lse [N,B,H] (kv_len [N,B] int32 optional): every rank
+        packs its own send buffer (one launch)."""
+        ops.dcp_pack_a2a_send(out, lse, self.payload, self.words, kv_len=kv_len)
 
     def recv(self):
         """Received buffers of all destinations: [dst, src, B, Hpr, D] and [dst, src, B, Hpr]."""
@@ -58,9 +59,9 @@ class StackedSplit:
         self.o_out = torch.empty_like(self.partial_o)
         self.stats_out = torch.empty_like(self.stats)
 
-    def pack(self, out: torch.Tensor, lse: torch.Tensor) -> None:
+    def pack(self, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
         ops.dcp_pack_a2a_send(out, lse, self.partial_o.permute(0, 3, 1, 2, 4),
-                              self.stats[..., 0].permute(0, 3, 1, 2))
+                              self.stats[..., 0].permute(0, 3, 1, 2), kv_len=kv_len)
 
     def exchange(self) -> None:
         """Stand-in for the all-to-all: o_out[dst, b, hl, src] = partial_o[src, b, hl, dst]."""

@@ -44,17 +44,30 @@
 /* to dst_o[p, b, hl, :] and dst_lse[p, b, hl].  Every stride is in BYTES.    */
 /* Bytes of the destination that no (b, h) addresses are left as they were   */
 /* ([P1] 实现拆解 item 3: stats slot 1 is never written).                    */
+/* kv_len (nullable, int32 per token, stride kl_b bytes): a token for which  */
+/* this rank owns no KV is sent as the neutral pair instead -- payload 0 and */
+/* LSE -inf ([P3] 实现拆解 item 3, fixup_zero_kv_rows).                       */
 /* ------------------------------------------------------------------------ */
 ORC_API void orc_pack(const uint8_t* src_o, int64_t so_b, int64_t so_h, int64_t so_d,
                       const uint8_t* src_lse, int64_t sl_b, int64_t sl_h,
                       uint8_t* dst_o, int64_t do_n, int64_t do_b, int64_t do_h, int64_t do_d,
                       uint8_t* dst_lse, int64_t dl_n, int64_t dl_b, int64_t dl_h,
+                      const uint8_t* kv_len, int64_t kl_b,
                       int64_t N, int64_t B, int64_t H, int64_t D, int64_t esize) {
     int64_t Hpr = H / N;
+    const float neg_inf = -INFINITY;
     for (int64_t b = 0; b < B; ++b) {
+        int32_t len = 1;
+        if (kv_len) memcpy(&len, kv_len + b * kl_b, 4);
         for (int64_t h = 0; h < H; ++h) {
             int64_t p = h / Hpr;
             int64_t hl = h % Hpr;
+            if (len == 0) {
+                for (int64_t d = 0; d < D; ++d)
+                    memset(dst_o + p * do_n + b * do_b + hl * do_h + d * do_d, 0, (size_t)esize);
+                memcpy(dst_lse + p * dl_n + b * dl_b + hl * dl_h, &neg_inf, 4);
+                continue;
+            }
             for (int64_t d = 0; d < D; ++d) {
                 memcpy(dst_o + p * do_n + b * do_b + hl * do_h + d * do_d,
                        src_o + b * so_b + h * so_h + d * so_d, (size_t)esize);

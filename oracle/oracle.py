@@ -59,6 +59,7 @@ def load_library(path: str):
     i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.orc_pack.argtypes = [vp, i64, i64, i64, vp, i64, i64,
                              vp, i64, i64, i64, i64, vp, i64, i64, i64,
+                             vp, i64,
                              i64, i64, i64, i64, i64]
     lib.orc_pack.restype = None
     lib.orc_combine.argtypes = [vp, vp, i64, i64, i64, c_int, vp, vp, vp, vp]
@@ -110,10 +111,12 @@ def to_f64(a: np.ndarray, dt: str) -> np.ndarray:
 # pack
 # --------------------------------------------------------------------------
 def pack(src_o: np.ndarray, src_lse: np.ndarray, dst_o: np.ndarray, dst_lse: np.ndarray, N: int,
-         lib=None) -> None:
+         lib=None, kv_len: np.ndarray | None = None) -> None:
     """Scatter one rank's [B,H,D] payload and [B,H] fp32 LSE into the per-peer
     views dst_o [N,B,H/N,D] and dst_lse [N,B,H/N] (any strides, written in
-    place).  Bit copy.  sglang PR #34651 report, 实现拆解 item 1."""
+    place).  Bit copy.  sglang PR #34651 report, 实现拆解 item 1.  With kv_len
+    ([B] int32), a token whose rank-local KV length is 0 is sent as the
+    neutral pair (0, -inf) (sglang PR #33926 report, 实现拆解 item 3)."""
     B, H, D = src_o.shape
     assert H % N == 0
     Hpr = H // N
@@ -121,9 +124,13 @@ def pack(src_o: np.ndarray, src_lse: np.ndarray, dst_o: np.ndarray, dst_lse: np.
     assert src_lse.shape == (B, H) and src_lse.itemsize == 4 and dst_lse.itemsize == 4
     assert src_o.itemsize == dst_o.itemsize
     assert dst_o.flags.writeable and dst_lse.flags.writeable
+    kv_ptr, kv_stride = None, 0
+    if kv_len is not None:
+        assert kv_len.dtype == np.int32 and kv_len.shape == (B,)
+        kv_ptr, kv_stride = _ptr(kv_len), kv_len.strides[0]
     _load(lib).orc_pack(_ptr(src_o), *src_o.strides, _ptr(src_lse), *src_lse.strides,
-                     _ptr(dst_o), *dst_o.strides, _ptr(dst_lse), *dst_lse.strides,
-                     N, B, H, D, src_o.itemsize)
+                        _ptr(dst_o), *dst_o.strides, _ptr(dst_lse), *dst_lse.strides,
+                        kv_ptr, kv_stride, N, B, H, D, src_o.itemsize)
 
 
 # --------------------------------------------------------------------------

@@ -62,6 +62,7 @@ def test_lse_pack_dim_and_status_strings():
 def pack(**kw):
     args = dict(src_o=A, so_R=0, so_B=512, so_H=64, src_lse=A, sl_R=0, sl_B=8, sl_H=1,
                 dst_o=A, do_R=0, do_N=256, do_B=128, do_H=64, dst_lse=A, dl_R=0, dl_N=4, dl_B=2, dl_H=1,
+                kv_len=None, kl_R=0, kl_B=1,
                 R=1, N=2, B=4, H=8, D=64, dtype=0, stream=None)
     args.update(kw)
     return _lib.lib().dcp_pack(*args.values())
@@ -90,6 +91,7 @@ def inplace(**kw):
     (dict(so_H=-1), STRIDE), (dict(dl_N=-4), STRIDE), (dict(do_R=-1), STRIDE),
     (dict(src_o=None), NULL), (dict(dst_lse=None), NULL),
     (dict(src_lse=A + 2), ALIGN), (dict(dst_o=A + 1, dtype=1), ALIGN), (dict(dst_o=A + 2, dtype=0), ALIGN),
+    (dict(kv_len=A + 2), ALIGN), (dict(kl_B=-1), STRIDE), (dict(kv_len=A, B=0), OK),
     (dict(H=1 << 25, N=1), SHAPE), (dict(D=1 << 27), SHAPE),
     (dict(B=0), OK), (dict(R=0), OK), (dict(B=0, src_o=None), OK),
 ])

@@ -36,8 +36,11 @@ MUTANTS = {
     "inplace_rank_index": ("l[(rank0 + j) * rows + r]", "l[j * rows + r]"),
     "no_single_rank_shortcut": ("        if (N == 1) {\n            g[r] = l[r];\n            for (int64_t d = 0; d < D; ++d) {\n                out[r * D + d] = o[r * D + d];",
                                 "        if (N == 0) {\n            g[r] = l[r];\n            for (int64_t d = 0; d < D; ++d) {\n                out[r * D + d] = o[r * D + d];"),
-    "lse_byte_swapped_peer": ("memcpy(dst_lse + p * dl_n + b * dl_b + hl * dl_h",
-                              "memcpy(dst_lse + hl * dl_n + b * dl_b + p * dl_h"),
+    "lse_byte_swapped_peer": ("memcpy(dst_lse + p * dl_n + b * dl_b + hl * dl_h, src_lse",
+                              "memcpy(dst_lse + hl * dl_n + b * dl_b + p * dl_h, src_lse"),
+    "neutral_lse_sign": ("const float neg_inf = -INFINITY;", "const float neg_inf = INFINITY;"),
+    "neutral_payload_kept": ("if (len == 0) {\n                for (int64_t d = 0; d < D; ++d)\n                    memset(",
+                             "if (len == 0) {\n                for (int64_t d = 0; d < 0; ++d)\n                    memset("),
     "max_not_subtracted": ("s += orc_pow_base(l[i * stride] - m, base2);",
                            "s += orc_pow_base(l[i * stride], base2);"),
 }
@@ -111,6 +114,16 @@ def pin_suite(lib):
     if not (np.array_equal(send[..., :D], out_t.view(B, N, Hpr, D).permute(1, 0, 2, 3).numpy())
             and np.array_equal(send[..., D], lse_t.view(B, N, Hpr).permute(1, 0, 2).numpy())):
         failed.append("pack_page_construction")
+    # pack with zero-KV tokens == pack of the explicitly neutralised inputs
+    kv = np.array([3, 0], np.int32)
+    o_n, l_n = out_t.numpy().copy(), lse_t.numpy().copy()
+    o_n[1], l_n[1] = 0.0, -np.inf
+    a = np.full((N, B, Hpr, D + 1), 5.0, np.float32)
+    b_ = np.full((N, B, Hpr, D + 1), 5.0, np.float32)
+    orc.pack(out_t.numpy(), lse_t.numpy(), a[..., :D], a[..., D], N, lib=lib, kv_len=kv)
+    orc.pack(o_n, l_n, b_[..., :D], b_[..., D], N)
+    if not np.array_equal(a.view(np.uint32), b_.view(np.uint32)):
+        failed.append("pack_neutral_rows")
     return failed
 
 

@@ -390,3 +390,33 @@ def test_pack_round_trip_through_exchange():
         for s in range(N):
             np.testing.assert_array_equal(recv[s, ..., :D], outs[s][:, r * Hpr:(r + 1) * Hpr])
             np.testing.assert_array_equal(recv[s, ..., D], lses[s][:, r * Hpr:(r + 1) * Hpr])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "f16"])
+def test_pack_zero_kv_tokens_become_neutral(dt):
+    """A token for which this rank owns no KV is sent as the neutral pair
+    (0, -inf): the same bytes as packing an output row of zeros and an LSE of
+    -inf (sglang PR #33926 report, 实现拆解 item 3, fixup_zero_kv_rows)."""
+    N, B, Hpr, D = 4, 6, 3, 40
+    H = N * Hpr
+    g = torch.Generator().manual_seed(3)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}[dt]
+    out = torch.randn(B, H, D, generator=g).to(tdt)
+    lse = torch.randn(B, H, generator=g)
+    kv = np.array([5, 0, 1, 0, 0, 9], np.int32)
+    o_np = out.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else out.numpy()
+    neutral_o = o_np.copy()
+    neutral_l = lse.numpy().copy()
+    neutral_o[kv == 0] = 0
+    neutral_l[kv == 0] = -np.inf
+    lpd = 4 // orc.ESIZE[dt]
+    npdt = {"bf16": np.uint16, "f32": np.float32, "f16": np.float16}[dt]
+    a = np.zeros((N, B, Hpr, D + lpd), npdt)
+    b = np.zeros((N, B, Hpr, D + lpd), npdt)
+    pa, wa = orc.interleaved_views_np(a, D, dt)
+    pb, wb = orc.interleaved_views_np(b, D, dt)
+    orc.pack(o_np, lse.numpy(), pa, wa, N, kv_len=kv)
+    orc.pack(neutral_o, neutral_l, pb, wb, N)
+    np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert np.all(np.isneginf(wa[:, 1])) and np.all(wa[:, 0] == lse.numpy().reshape(B, N, Hpr).transpose(1, 0, 2)[:, 0])
+
