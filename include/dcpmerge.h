@@ -27,6 +27,11 @@
  *   - Outputs must not overlap inputs (except where stated) or each other.
  *   - Errors are detected on the host before anything is enqueued: on any
  *     error nothing is written.  A zero-sized call (R, B or T = 0) is DCP_OK.
+ *   - Size limits: the heads of one token (H, or Hpr for the combine) times
+ *     (D * element size / 32 + 1) must not exceed 2^25, H <= 2^24 and
+ *     D * element size <= 2^28 bytes; otherwise DCP_ERR_SHAPE.  R, B and T
+ *     are limited only by memory: the library splits them over several
+ *     launches.
  *   - Leading dimension R ("R independent problems") is an extension for
  *     running several ranks' calls in one launch, e.g. all N simulated ranks
  *     stacked in one GPU's memory.  R = 1 is the single call the pages

@@ -10,7 +10,7 @@
 
 namespace {
 
-using dcp::kMaxRowsPerLaunch;
+using dcp::max_units_per_launch;
 
 int esize_of(int dtype) {
     switch (dtype) {
@@ -29,11 +29,13 @@ bool nonneg(std::initializer_list<int64_t> xs) {
     return true;
 }
 
-// Shapes must keep every per-launch index within 32 bits even after the
-// launchers split the work along R, B and T.
+// The launchers split the work along R, B and T, never inside one token:
+// the row-steps of one token (at most H * (row_bytes / 32 + 1) for any
+// kernel) must fit in one launch of the kernel with the fewest row-steps per
+// workgroup (4), so that every launch stays within its index and grid limits.
 bool shape_fits(int64_t H, int64_t row_bytes) {
     if (H > (int64_t(1) << 24) || row_bytes > (int64_t(1) << 28)) return false;
-    return H * (row_bytes / 32 + 1) <= kMaxRowsPerLaunch;
+    return H * (row_bytes / 32 + 1) <= max_units_per_launch(4);
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH; }

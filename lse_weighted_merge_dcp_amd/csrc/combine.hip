@@ -320,11 +320,12 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
     const int64_t chunks = a.D * DT::esize / V;
     const int64_t steps = (chunks + LPR - 1) / LPR;
     const int64_t per_r = a.B * a.Hpr * steps;
-    int64_t r_chunk = per_r > 0 ? kMaxRowsPerLaunch / per_r : a.R;
+    const int64_t lim = max_units_per_launch(RPB);
+    int64_t r_chunk = per_r > 0 ? lim / per_r : a.R;
     int64_t b_chunk = a.B;
     if (r_chunk < 1) {
         r_chunk = 1;
-        b_chunk = kMaxRowsPerLaunch / (a.Hpr * steps);
+        b_chunk = lim / (a.Hpr * steps);
     }
     for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
         const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;

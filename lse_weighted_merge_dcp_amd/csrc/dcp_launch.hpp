@@ -76,4 +76,15 @@ int pick_vec_bytes(int64_t row_bytes, int esize, const int64_t* addrs_and_stride
 // row-steps (keeps every in-kernel index within 32 bits).
 constexpr int64_t kMaxRowsPerLaunch = int64_t(1) << 30;
 
+// The grid size of a launch, counted in work-items, must fit in 32 bits; with
+// 256-lane workgroups, at most 2^23 of them per launch (2^31 work-items).
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 23;
+
+// Row-steps one launch may take when each 256-lane workgroup takes
+// units_per_block of them: both limits above hold.
+constexpr int64_t max_units_per_launch(int64_t units_per_block) {
+    return kMaxBlocksPerLaunch * units_per_block < kMaxRowsPerLaunch ? kMaxBlocksPerLaunch * units_per_block
+                                                                     : kMaxRowsPerLaunch;
+}
+
 }  // namespace dcp

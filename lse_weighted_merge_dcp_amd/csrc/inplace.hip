@@ -210,7 +210,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR);
     const int64_t chunks = a.D * DT::esize / V;
     const int64_t steps = (chunks + LPR - 1) / LPR;
-    const int64_t t_chunk = kMaxRowsPerLaunch / (a.H * steps);
+    const int64_t t_chunk = max_units_per_launch(RPB) / (a.H * steps);
     for (int64_t t0 = 0; t0 < a.T; t0 += t_chunk) {
         const int64_t nt = t0 + t_chunk <= a.T ? t_chunk : a.T - t0;
         InplK k;

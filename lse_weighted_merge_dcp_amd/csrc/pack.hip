@@ -206,11 +206,12 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
     const int64_t Q = a.Hpr * W / 16;
     const int64_t S = (Q + 63) / 64;
     const int64_t per_r = a.B * N * S;
-    int64_t r_chunk = kMaxRowsPerLaunch / per_r;
+    const int64_t lim = max_units_per_launch(4 * kStreamU);
+    int64_t r_chunk = lim / per_r;
     int64_t b_chunk = a.B;
     if (r_chunk < 1) {
         r_chunk = 1;
-        b_chunk = kMaxRowsPerLaunch / (N * S);
+        b_chunk = lim / (N * S);
     }
     for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
         const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;
@@ -252,11 +253,13 @@ hipError_t run(const PackArgs& a, hipStream_t stream) {
     const int64_t steps = (chunks + LPR - 1) / LPR;
     const int64_t per_r = a.B * a.H * steps;
     // split along R, then along B, so one launch stays within 32-bit indices
-    int64_t r_chunk = per_r > 0 ? kMaxRowsPerLaunch / per_r : a.R;
+    // and grid sizes
+    const int64_t lim = max_units_per_launch(RPB);
+    int64_t r_chunk = per_r > 0 ? lim / per_r : a.R;
     int64_t b_chunk = a.B;
     if (r_chunk < 1) {
         r_chunk = 1;
-        b_chunk = kMaxRowsPerLaunch / (a.H * steps);
+        b_chunk = lim / (a.H * steps);
     }
     for (int64_t r0 = 0; r0 < a.R; r0 += r_chunk) {
         const int64_t nr = r0 + r_chunk <= a.R ? r_chunk : a.R - r0;

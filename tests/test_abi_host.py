@@ -93,6 +93,7 @@ def inplace(**kw):
     (dict(src_lse=A + 2), ALIGN), (dict(dst_o=A + 1, dtype=1), ALIGN), (dict(dst_o=A + 2, dtype=0), ALIGN),
     (dict(kv_len=A + 2), ALIGN), (dict(kl_B=-1), STRIDE), (dict(kv_len=A, B=0), OK),
     (dict(H=1 << 25, N=1), SHAPE), (dict(D=1 << 27), SHAPE),
+    (dict(H=1 << 22, N=1), SHAPE), (dict(H=1 << 11, N=1, D=1 << 20), SHAPE),   # one token's rows > 2^25
     (dict(B=0), OK), (dict(R=0), OK), (dict(B=0, src_o=None), OK),
 ])
 def test_pack_validation(kw, code):
@@ -102,6 +103,7 @@ def test_pack_validation(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), DTYPE), (dict(lse_base=2), BASE), (dict(lse_base=-1), BASE),
     (dict(N=0), SHAPE), (dict(Hpr=0), SHAPE), (dict(D=0), SHAPE), (dict(B=-2), SHAPE), (dict(N=1 << 21), SHAPE),
+    (dict(Hpr=1 << 22), SHAPE),
     (dict(ro_N=-1), STRIDE), (dict(ol_B=-4), STRIDE),
     (dict(recv_o=None), NULL), (dict(out=None), NULL), (dict(recv_lse=None), NULL),
     (dict(recv_lse=A + 1), ALIGN), (dict(out_lse=A + 2), ALIGN), (dict(out=A + 1, dtype=2), ALIGN),
@@ -114,6 +116,7 @@ def test_combine_validation(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=9), DTYPE), (dict(lse_base=5), BASE),
     (dict(P=0), SHAPE), (dict(P=3), SHAPE), (dict(rank0=1), SHAPE), (dict(rank0=-1), SHAPE), (dict(T=-1), SHAPE),
+    (dict(H=1 << 22), SHAPE),
     (dict(h0=-1), HRANGE), (dict(h0=4, h1=4), HRANGE), (dict(h1=9), HRANGE), (dict(h0=5, h1=3), HRANGE),
     (dict(p_T=-1), STRIDE), (dict(ol_H=-1), STRIDE),
     (dict(partial=None), NULL), (dict(lse=None), NULL),
