@@ -1,6 +1,6 @@
 """Benchmark of the DCP partial-merge path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload dsv3|longctx|split|tiny|kimi] [--B 64]
+    python bench.py [--steps K] [--warmup W] [--workload dsv3|longctx|split|tiny|kimi|kimi-rs] [--B 64]
 
 Default workload: DeepSeek-V3-shaped MLA decode -- N=8 simulated DCP ranks,
 B=64 tokens, H=128 heads (16 per rank), D=512 (kv_lora_rank), bf16 partials,
@@ -17,7 +17,16 @@ bytes (what the method must move: (3N+1)(D*e+4) bytes per (token, head) for
 pack + combine), microseconds per layer, the roofline entry of the dominant
 kernel (per-launch duration from HIP events on the launch stream, over a
 replayed graph of that kernel's launches) and the CPU oracle timed on a
-bounded sample.
+bounded sample.  Beside them: the p10/p50/p90 step time, the rate of a plain
+2 GiB device-to-device copy measured in the same run (the practical ceiling),
+and for the pack + combine workloads the per-rank share (one rank's pack and
+one destination's combine at their real shapes) and the cache-resident step
+(one layer's buffers reused by every layer).
+
+Other workloads: longctx (N=16, H=128, bf16, --B 1..512), split (peer-inside
+split layout, fp16), tiny (N=2 fp32), kimi (in-place merge over 8 ranks'
+[16384, 96, 512] fp32 partials), kimi-rs (the same merge, reduce-scatter
+flavour: each rank's head slice, no partial write-back).
 
 Other modes:
   --counter-run       run a 1 GiB plain copy and a few launches of each kernel
@@ -33,6 +42,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -115,6 +125,30 @@ class A2AWorkload:
     def combine(self, l):
         k = l % self.distinct
         self.stk[k].combine(is_lse_base_on_e=not self.w.base2, out=self.out[k], out_lse=self.glse[k])
+
+    def pack_rank0(self, l):
+        k = l % self.distinct
+        self.stk[k].pack_rank(0, self.src[k][0], self.lse[k][0])
+
+    def combine_dest0(self, l):
+        k = l % self.distinct
+        self.stk[k].combine_dest(0, not self.w.base2, out=self.out[k][0], out_lse=self.glse[k][0])
+
+    def per_rank(self):
+        """One rank's pack and one destination's combine at their real shapes
+        (1/N of the all-rank launches), over the same distinct layer buffers."""
+        N = self.w.N
+        return [("pack", self.bytes_pack // N, [lambda l=l: self.pack_rank0(l) for l in range(self.layers)]),
+                ("combine", self.bytes_combine // N,
+                 [lambda l=l: self.combine_dest0(l) for l in range(self.layers)])]
+
+    def hot_launches(self):
+        """The step with one layer's buffers reused by every layer (cache-resident)."""
+        fns = []
+        for _ in range(self.layers):
+            fns.append(lambda: self.pack(0))
+            fns.append(lambda: self.combine(0))
+        return fns
 
     def step_launches(self):
         fns = []
@@ -238,9 +272,108 @@ class InplaceWorkload:
                     done, w.B, t_total)}
 
 
+class ReduceScatterWorkload:
+    """Reduce-scatter flavour of the in-place merge (Kimi-K3 cached-extend
+    shape): every rank's head slice of the merged output straight from all N
+    partials, with no write-back of scaled partials.  It is the out-of-place
+    combine over strided views of the partial stack: rank r's call reads
+    heads [r*Hpr, (r+1)*Hpr) of every partial; the N ranks' calls run stacked
+    along the leading R dimension, in one launch."""
+
+    def __init__(self, B, dev):
+        import torch
+
+        from lse_weighted_merge_dcp_amd import synth
+
+        w = synth.WORKLOADS["kimi"]
+        if B is not None:
+            w = w.with_batch(B)
+        self.w, self.dev, self.layers = w, dev, 1
+        t0 = time.time()
+        self.part = synth.kimi_partial_device(w, dev)
+        self.lse_np = synth.kimi_lse(w)
+        self.lse = torch.from_numpy(self.lse_np).to(dev)
+        self.out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=dev)
+        self.glse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
+        row = 4 * w.D
+        self.bytes_call = w.B * w.H * (w.N * (row + 4) + row + 4)
+        self.dtype = "f32"
+
+    def run(self):
+        from lse_weighted_merge_dcp_amd import sim
+
+        sim.reduce_scatter_merge(self.part, self.lse, out=self.out, out_lse=self.glse)
+
+    def kernels(self):
+        return [("combine", self.bytes_call, [self.run])]
+
+    def step_bytes(self):
+        return self.bytes_call
+
+    def config(self):
+        w = self.w
+        return {"workload": "Kimi-K3-shaped cached-extend merge, reduce-scatter flavour: N=8 ranks' partials "
+                            "[%d, %d, %d] fp32, base-e LSE with 0.1%% NaN/inf, each rank's %d-head slice of the "
+                            "output, no partial write-back" % (w.B, w.H, w.D, w.H // w.N),
+                "N": w.N, "T": w.B, "H": w.H, "D": w.D}
+
+    def cpu_sample(self, budget_s):
+        from oracle import oracle as orc
+
+        w = self.w
+        tblk = 64
+        done, t_total = 0, 0.0
+        while t_total < budget_s and done + tblk <= w.B:
+            part = self.part[:, done:done + tblk].cpu().numpy()
+            lse = self.lse_np[:, done:done + tblk]
+            t0 = time.perf_counter()
+            orc.combine(part, lse, "f32", False)
+            t_total += time.perf_counter() - t0
+            done += tblk
+        per_tok = self.bytes_call / w.B
+        return {"value": per_tok * done / t_total / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+                "sample": "first %d of %d tokens (all 8 ranks, 96 heads), %.1f s of CPU time, fp64" % (
+                    done, w.B, t_total)}
+
+
 # --------------------------------------------------------------------------
 # timing
 # --------------------------------------------------------------------------
+def copy_ceiling_gbs(dev, nbytes=2 << 30, reps=10):
+    """Achievable HBM rate of a plain device-to-device copy of nbytes (read
+    nbytes + write nbytes), timed with HIP events: the practical ceiling."""
+    import torch
+
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    torch.cuda.empty_cache()
+    times.sort()
+    return 2 * nbytes / times[len(times) // 2] / 1e9
+
+
+def percentiles(xs):
+    xs = sorted(xs)
+
+    def q(f):
+        return xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+
+    return {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4)}
+
+
 def per_launch_us(launches, reps, restore=None):
     """Average duration of one launch: a HIP graph of the given launches is
     replayed `reps` times between two HIP events recorded on the stream the
@@ -279,7 +412,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3", choices=["dsv3", "longctx", "split", "tiny", "kimi"])
+    ap.add_argument("--workload", default="dsv3", choices=["dsv3", "longctx", "split", "tiny", "kimi", "kimi-rs"])
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--layers", type=int, default=61)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
@@ -303,6 +436,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "kimi":
         wl = InplaceWorkload(args.B, dev)
+    elif args.workload == "kimi-rs":
+        wl = ReduceScatterWorkload(args.B, dev)
     else:
         wl = A2AWorkload(args.workload, args.B, args.layers, dev)
 
@@ -314,6 +449,9 @@ def main():
     if args.workload == "kimi":
         step = [wl.run]
         restore = wl.restore
+    elif args.workload == "kimi-rs":
+        step = [wl.run]
+        restore = None
     else:
         step = wl.step_launches()
         restore = None
@@ -338,23 +476,30 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, synchronised on both sides
+    # (HIP events between the replays give the per-step spread)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
     if restore is None:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            ev[2 * i].record()
             graph.replay()
+            ev[2 * i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     else:
         # the in-place call destroys its input: restore it (untimed) before each step
         wall = 0.0
-        for _ in range(args.steps):
+        for i in range(args.steps):
             restore()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
+            ev[2 * i].record()
             graph.replay()
+            ev[2 * i + 1].record()
             torch.cuda.synchronize()
             wall += time.perf_counter() - t0
+    step_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
     ms_per_step = wall / args.steps * 1e3
     gbs = wl.step_bytes() / (wall / args.steps) / 1e9
 
@@ -363,6 +508,21 @@ def main():
     for name, nbytes, launches in wl.kernels():
         us, _ = per_launch_us(launches, reps=max(3, args.steps // 4), restore=restore)
         kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9}
+    extra = {}
+    layers = getattr(wl, "layers", 1)
+    if hasattr(wl, "per_rank"):
+        pr = {}
+        for name, nbytes, launches in wl.per_rank():
+            us, _ = per_launch_us(launches, reps=max(3, args.steps // 4))
+            pr[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
+                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        pr["us_per_layer"] = round(sum(v["us_per_launch"] for v in pr.values()), 3)
+        extra["per_rank"] = pr
+        us, _ = per_launch_us(wl.hot_launches(), reps=max(3, args.steps // 4))
+        extra["hot"] = {"us_per_layer": round(2 * us, 3),
+                        "GBps": round(wl.bytes_layer / (2 * us * 1e-6) / 1e9, 1),
+                        "note": "one layer's buffers reused by all layers (cache-resident)"}
+    ceiling = copy_ceiling_gbs(dev)
     dom = max(kinfo, key=lambda k: kinfo[k]["us_per_launch"])
     achieved = kinfo[dom]["GBps"]
     traffic = load_traffic(args.workload, wl, dom)
@@ -371,7 +531,6 @@ def main():
     if args.cpu_budget > 0:
         cpu = wl.cpu_sample(args.cpu_budget)
 
-    layers = getattr(wl, "layers", 1)
     res = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -388,9 +547,13 @@ def main():
         "config": wl.config(),
         "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "us_per_layer": round(ms_per_step * 1e3 / layers, 3),
+        "step_ms": percentiles(step_ms),
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "pct_of_copy_ceiling": round(100.0 * gbs / ceiling, 2),
         "bytes_per_step": wl.step_bytes(),
         "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
                     for k, v in kinfo.items()},
+        **extra,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
@@ -451,7 +614,7 @@ def summarize_counters(directory, workload):
         by.setdefault((name, cn), []).append(val)
 
     def pick(pattern, cn):
-        vals = [v for (k, c), vs in by.items() if pattern in k and c == cn for v in vs]
+        vals = [v for (k, c), vs in by.items() if re.search(pattern, k) and c == cn for v in vs]
         return sum(vals) / len(vals) if vals else None
 
     copy_bytes = 1 << 30      # torch.neg over 2^28 fp32: 1 GiB read, 1 GiB written
@@ -464,7 +627,8 @@ def summarize_counters(directory, workload):
     out = {"kernel_source": kernel_source_hash(), "workload": workload,
            "copy_reference": {"bytes": copy_bytes, "FETCH_SIZE": f_copy, "WRITE_SIZE": w_copy,
                               "fetch_scale": fs, "write_scale": ws}, "kernels": {}}
-    for kname, pat in (("pack", "pack_kernel"), ("combine", "combine_"), ("inplace", "inplace_kernel")):
+    for kname, pat in (("pack", r"\bpack_(stream_)?kernel"), ("combine", r"\bcombine_(wave_)?kernel"),
+                       ("inplace", r"\binplace_kernel")):
         f = pick(pat, "FETCH_SIZE")
         wv = pick(pat, "WRITE_SIZE")
         if f is None or wv is None:

@@ -231,13 +231,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 }
 
 
-// Row-per-wave variant (LPR = 64, 16-byte vectors, fixed N <= 16): the row
-// is wave-uniform, so the N peer rows are read with raw buffer loads that
-// share one VGPR lane offset (the per-peer offsets live in scalar registers)
-// and the weights are moved to scalar registers.  That keeps the kernel at
-// about 64 VGPRs, i.e. 8 waves per SIMD.  Requires every peer offset
-// (N-1) * r_N + row bytes to fit in 31 bits (checked by the launcher).
-template <typename DT, int NT>
+// Row-per-wave variant (LPR = 64, 16-byte vectors, fixed N <= 16).  The
+// row is wave-uniform, so each peer row's base address sits in scalar
+// registers and all N loads share one VGPR lane offset; the weights move to
+// scalar registers too.  That keeps the kernel at 44 VGPRs for N = 8.  The
+// payload is read with the nontemporal hint (each received row is read
+// once), which also keeps it from displacing lines the next launch reuses.
+//
+// HOIST issues the payload loads right after the LSE load, so the LSE
+// reduction runs while the payload is in flight: one memory round trip per
+// wave instead of two.  That wins when the launch is latency-bound (few
+// rows, every wave resident at once); on large launches loading after the
+// weights measured faster, and the launcher picks by size.
+template <typename DT, int NT, bool HOIST>
 __global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
     using C = Cvt<DT, 16>;
     constexpr int EPV = C::n;
@@ -257,11 +263,20 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
     const char* rbase = k.recv + r * k.r_R + b * k.r_B + hl * k.r_H;
     const char* lbase = k.rlse + r * k.rl_R + b * k.rl_B + hl * k.rl_H;
     char* obase = k.out + r * k.o_R + b * k.o_B + hl * k.o_H;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)rbase, (short)0, (int)0xFFFFFFFF, (int)0x00020000);
+
+    const uint32_t c = seg * 64u + lane;
+    const bool on = c < k.chunks;
+    // lanes past the row end read its last chunk again (never stored), so
+    // the loads need no branch and the LSE wait never covers them
+    const uint32_t voff = (on ? c : k.chunks - 1u) * 16u;
+    Vec<16> x[NT];
 
     float lj = -INFINITY;
     if (j < (uint32_t)NT) lj = load_f32(lbase + (int64_t)j * k.rl_N);
+    if constexpr (HOIST) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) x[i] = gload16<true>(wave_addr(rbase + i * k.r_N), voff);
+    }
     LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj), base2);
     float w = 0.0f;
     if (st.live) {
@@ -275,44 +290,46 @@ __global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
         ((wi[I] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, row_bcast<I>(w))))),
          ...);
     }(std::make_integer_sequence<int, NT>{});
+    if constexpr (!HOIST) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) x[i] = gload16<true>(wave_addr(rbase + i * k.r_N), voff);
+    }
 
-    {
-        const uint32_t c = seg * 64u + lane;
-        if (c < k.chunks) {
-            const int voff = (int)(c * 16u);
-            Vec<16> x[NT];
+    float acc[EPV];
 #pragma unroll
-            for (int i = 0; i < NT; ++i) x[i] = buffer_vload16(rsrc, voff, (int)((uint32_t)i * (uint32_t)k.r_N));
-            float acc[EPV];
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+    for (int i = 0; i < NT; ++i) {
+        float f[EPV];
+        C::unpack(x[i], f);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                float f[EPV];
-                C::unpack(x[i], f);
+        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], f[e], acc[e]);
+    }
+    bool bad = false;
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], f[e], acc[e]);
-            }
-            bool bad = false;
+    for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        // a non-finite payload value: re-form the sum with the guards (the
+        // rows are read again rather than kept live, which would cost VGPRs)
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
-            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+        for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+        for (int i = 0; i < NT; ++i) {
+            float f[EPV];
+            C::unpack(gload16<false>(wave_addr(rbase + i * k.r_N), voff), f);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) {
-                    float f[EPV];
-                    C::unpack(buffer_vload16(rsrc, voff, (int)((uint32_t)i * (uint32_t)k.r_N)), f);
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
-                }
-            }
-            vstore<16>(obase + voff, C::pack(acc));
+            for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
         }
     }
+    if (on) vstore<16>(obase + voff, C::pack(acc));
     if (k.olse != nullptr && lane == 0 && seg == 0)
         *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
 }
+
+// Launches with at most this many row tasks take the HOIST order (measured
+// crossover on MI355X between the latency-bound and the bandwidth-bound
+// regime of the row-per-wave kernel).
+constexpr int64_t kHoistMaxRows = 2048;
 
 template <typename DT, int V, int LPR, int NT>
 hipError_t run(const CombineArgs& a, hipStream_t stream) {
@@ -352,13 +369,11 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             k.f_steps = make_fastdiv(k.steps);
             k.base2 = a.base2 ? 1 : 0;
             const int64_t blocks = (rows + RPB - 1) / RPB;
-            const bool wave_path = V == 16 && LPR == 64 && NT > 0 &&
-                                   (a.N - 1) * a.r_N + a.D * DT::esize < (int64_t(1) << 31);
             if constexpr (V == 16 && LPR == 64 && NT > 0) {
-                if (wave_path) {
-                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                if (rows <= kHoistMaxRows) {
+                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, true>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
                 } else {
-                    hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, false>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
                 }
             } else {
                 hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);

@@ -61,13 +61,27 @@ template <> __device__ __forceinline__ void vstore<2>(char* p, const Vec<2>& v) 
     *reinterpret_cast<uint16_t*>(p) = v.h;
 }
 
-// 16 bytes from a raw buffer: base in the descriptor, per-lane byte offset
-// voff and a wave-uniform byte offset soff (both below 2^31).
-__device__ __forceinline__ Vec<16> buffer_vload16(__amdgpu_buffer_rsrc_t rsrc, int voff, int soff) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 t = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
+// A wave-uniform address held in scalar registers: loads from it plus a
+// 32-bit per-lane offset take the scalar-base form of the global load (one
+// VGPR of offset for any number of rows, no 64-bit address arithmetic per
+// lane).  p must be the same for every lane of the wave.
+__device__ __forceinline__ uint64_t wave_addr(const char* p) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// 16 bytes at base + off (global memory, 4-byte aligned); NTL marks the line
+// as read once.
+typedef const u32x4_a4 __attribute__((address_space(1))) g_u32x4_a4;
+template <bool NTL>
+__device__ __forceinline__ Vec<16> gload16(uint64_t base, uint32_t off) {
+    g_u32x4_a4* p = (g_u32x4_a4*)(base + off);
+    u32x4_a4 x;
+    if constexpr (NTL) x = __builtin_nontemporal_load(p); else x = *p;
     Vec<16> v;
-    v.w[0] = t.x; v.w[1] = t.y; v.w[2] = t.z; v.w[3] = t.w;
+    v.w[0] = x.x; v.w[1] = x.y; v.w[2] = x.z; v.w[3] = x.w;
     return v;
 }
 

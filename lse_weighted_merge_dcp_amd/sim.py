@@ -37,9 +37,18 @@ class StackedInterleaved:
         packs its own send buffer (one launch)."""
         ops.dcp_pack_a2a_send(out, lse, self.payload, self.words, kv_len=kv_len)
 
+    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor) -> None:
+        """Rank r's own pack at its real shape: out [B,H,D], lse [B,H]."""
+        ops.dcp_pack_a2a_send(out, lse, self.payload[r], self.words[r])
+
     def recv(self):
         """Received buffers of all destinations: [dst, src, B, Hpr, D] and [dst, src, B, Hpr]."""
         return self.payload.transpose(0, 1), self.words.transpose(0, 1)
+
+    def combine_dest(self, p: int, is_lse_base_on_e: bool, out=None, out_lse=None):
+        """Destination p's own combine at its real shape (its received [N, B, Hpr, D])."""
+        ro, rl = self.recv()
+        return ops.dcp_lse_combine(ro[p], rl[p], is_lse_base_on_e=is_lse_base_on_e, out=out, out_lse=out_lse)
 
     def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None):
         ro, rl = self.recv()
@@ -63,6 +72,10 @@ class StackedSplit:
         ops.dcp_pack_a2a_send(out, lse, self.partial_o.permute(0, 3, 1, 2, 4),
                               self.stats[..., 0].permute(0, 3, 1, 2), kv_len=kv_len)
 
+    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor) -> None:
+        """Rank r's own pack at its real shape: out [B,H,D], lse [B,H]."""
+        ops.dcp_pack_a2a_send(out, lse, self.partial_o[r].permute(2, 0, 1, 3), self.stats[r][..., 0].permute(2, 0, 1))
+
     def exchange(self) -> None:
         """Stand-in for the all-to-all: o_out[dst, b, hl, src] = partial_o[src, b, hl, dst]."""
         self.o_out.copy_(self.partial_o.permute(3, 1, 2, 0, 4))
@@ -76,3 +89,34 @@ class StackedSplit:
         ro, rl = self.recv()
         return ops.dcp_lse_combine(ro, rl, is_lse_base_on_e=is_lse_base_on_e, return_lse=return_lse,
                                    out=out, out_lse=out_lse)
+
+    def combine_dest(self, p: int, is_lse_base_on_e: bool, out=None, out_lse=None):
+        """Destination p's own combine at its real shape (its received [N, B, Hpr, D])."""
+        ro, rl = self.recv()
+        return ops.dcp_lse_combine(ro[p], rl[p], is_lse_base_on_e=is_lse_base_on_e, out=out, out_lse=out_lse)
+
+
+def reduce_scatter_merge(partial: torch.Tensor, lse: torch.Tensor, out=None, out_lse=None):
+    """Reduce-scatter flavour of the in-place merge for all N ranks at once.
+
+    partial [N, T, H, D] and lse [N, T, H] hold every rank's partial result.
+    Rank r owns heads [r*H/N, (r+1)*H/N) and merges them from all N partials
+    without writing scaled partials back: the all-reduce followed by a head
+    slice in the code excerpt of cp_lse_ag_out_rs_mha (sglang PR #34213
+    report), done as a one-shot reduce-scatter.
+    The N ranks' out-of-place combines over strided views run stacked along
+    the leading R dimension in one launch.  Returns out [T, H, D] (rank r's
+    slice at heads r*H/N...) and the global LSE [T, H]."""
+    N, T, H, D = partial.shape
+    assert H % N == 0 and tuple(lse.shape) == (N, T, H)
+    assert partial.is_contiguous() and lse.is_contiguous()
+    Hpr = H // N
+    if out is None:
+        out = torch.empty((T, H, D), dtype=partial.dtype, device=partial.device)
+    if out_lse is None:
+        out_lse = torch.empty((T, H), dtype=torch.float32, device=partial.device)
+    ops.dcp_lse_combine(partial.view(N, T, N, Hpr, D).permute(2, 0, 1, 3, 4),
+                        lse.view(N, T, N, Hpr).permute(2, 0, 1, 3), is_lse_base_on_e=True,
+                        out=out.view(T, N, Hpr, D).permute(1, 0, 2, 3),
+                        out_lse=out_lse.view(T, N, Hpr).permute(1, 0, 2))
+    return out, out_lse

@@ -159,6 +159,34 @@ def test_general_shapes(dt, N, D):
             check_lse(gg[r].cpu().numpy(), gr)
 
 
+@pytest.mark.parametrize("dt,N,D", [("bf16", 8, 400), ("f16", 16, 384), ("f32", 4, 1000), ("bf16", 2, 512)])
+@pytest.mark.parametrize("B", [5, 300])
+def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
+    """Rows of 768 bytes and more take the row-per-wave kernel: at B = 5 in
+    the latency order (payload loads issued before the LSE reduction), at
+    B = 300 (2400 rows or more) in the bandwidth order.  Rows that are not a
+    multiple of 64 16-byte chunks leave idle lanes in their last segment;
+    NaN and +-inf planted in the payload force the guarded re-read; special
+    LSE values and an all-neutral row are mixed in."""
+    say("row-per-wave", dt, N, D, B)
+    Hpr = 8
+    g = torch.Generator().manual_seed(N * 7 + D + B)
+    o = synth.to_storage(torch.randn(N, B, Hpr, D, generator=g), dt)
+    rng = np.random.default_rng(N + D + B)
+    lse = rng.normal(0, 4, size=(N, B, Hpr)).astype(np.float32)
+    for k in range(40):
+        lse[rng.integers(N), rng.integers(B), rng.integers(Hpr)] = [np.nan, np.inf, -np.inf][k % 3]
+    lse[:, 0, 0] = -np.inf
+    special_o = synth.to_storage(torch.tensor([math.nan, math.inf, -math.inf]), dt)
+    for k in range(100):
+        o[rng.integers(N), rng.integers(B), rng.integers(Hpr), rng.integers(D)] = special_o[k % 3]
+    base2 = B % 2 == 0
+    out, gg = ops.dcp_lse_combine(to_dev(o, dt, DEV), torch.from_numpy(lse).to(DEV), is_lse_base_on_e=not base2)
+    ref, gr, mag, _ = orc.combine(o, lse, dt, base2)
+    check_out(decode(to_host(out, dt), dt), ref, mag, dt)
+    check_lse(gg.cpu().numpy(), gr)
+
+
 def test_single_rank_identity_keeps_nan_and_inf_bits():
     o = np.random.default_rng(0).normal(size=(1, 3, 2, 64)).astype(np.float32)
     o[0, 0, 0, :3] = [np.nan, np.inf, -np.inf]

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from lse_weighted_merge_dcp_amd import ops, synth
+from lse_weighted_merge_dcp_amd import ops, sim, synth
 from oracle import oracle as orc
 
 from helpers import check_lse, check_out, check_scaled, decode, say, to_dev, to_host
@@ -100,12 +100,22 @@ def test_reduce_scatter_flavour_through_strided_combine():
     scaled, ref, gr, mag = orc.inplace(inp["out"], inp["lse"], "f32", False, h0=h0, h1=h1)
     check_out(rs.cpu().numpy(), ref, mag, "f32")
     check_lse(g.cpu().numpy(), gr)
+    # all 8 ranks' slices stacked along R in one launch (the benchmarked form),
+    # with every special LSE value planted
+    lse_np = inp["lse"].copy()
+    lse_np[0, 0, 0] = np.nan; lse_np[3, 1, 13] = np.inf; lse_np[:, 2, 30] = -np.inf; lse_np[5, 4, 95] = -np.inf
+    out, g = sim.reduce_scatter_merge(part, torch.from_numpy(lse_np).to(DEV))
+    _, ref, gr, mag = orc.inplace(inp["out"], lse_np, "f32", False)
+    check_out(out.cpu().numpy(), ref, mag, "f32")
+    check_lse(g.cpu().numpy(), gr)
 
 
 def test_inplace_full_size_sampled():
-    """8 x [16384, 96, 512] fp32 partials (24 GiB) merged in place in one call,
-    in the launch configuration the benchmark times; 3000 sampled (t, h) rows
-    are checked (scaled partials of all ranks, merged row, G)."""
+    """8 x [16384, 96, 512] fp32 partials (24 GiB) merged in one call, in the
+    launch configurations the benchmark times: first the reduce-scatter
+    flavour (every rank's head slice, stacked; the partials must stay
+    untouched), then in place; 3000 sampled (t, h) rows are checked (scaled
+    partials of all ranks, merged row, G) for both."""
     w = synth.WORKLOADS["kimi"]
     say("inplace full size", w.describe())
     part = synth.kimi_partial_device(w, DEV)
@@ -120,6 +130,13 @@ def test_inplace_full_size_sampled():
     ts = np.concatenate([ts, sp[:, 1]]); hs = np.concatenate([hs, sp[:, 2]])
     ti, hi = torch.from_numpy(ts).to(DEV), torch.from_numpy(hs).to(DEV)
     before = part[:, ti, hi].cpu().numpy()             # [N, S, D] inputs of the sampled rows
+    # reduce-scatter flavour first (it leaves the partials untouched)
+    rs_out, rs_g = sim.reduce_scatter_merge(part, lse)
+    torch.cuda.synchronize()
+    rs_got_out = rs_out[ti, hi].cpu().numpy()
+    rs_got_g = rs_g[ti, hi].cpu().numpy()
+    assert np.array_equal(part[:, ti, hi].cpu().numpy().view(np.uint32), before.view(np.uint32))
+    del rs_out, rs_g
     out, g = ops.cp_lse_combine_inplace(part, lse, return_lse=True)
     torch.cuda.synchronize()
     after = part[:, ti, hi].cpu().numpy()
@@ -130,5 +147,7 @@ def test_inplace_full_size_sampled():
     check_scaled(after, scaled.reshape(w.N, S, w.D), "f32")
     check_out(got_out, ref.reshape(S, w.D), mag.reshape(S, w.D), "f32")
     check_lse(got_g, gr.reshape(S))
+    check_out(rs_got_out, ref.reshape(S, w.D), mag.reshape(S, w.D), "f32")
+    check_lse(rs_got_g, gr.reshape(S))
     del part, out
     torch.cuda.empty_cache()
