@@ -242,16 +242,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 // reduction runs while the payload is in flight: one memory round trip per
 // wave instead of two.  That wins when the launch is latency-bound (few
 // rows, every wave resident at once); on large launches loading after the
-// weights measured faster, and the launcher picks by size.
-template <typename DT, int NT, bool HOIST>
-__global__ __launch_bounds__(256) void combine_wave_kernel(const CombK k) {
+// weights measured faster, and the launcher picks by size.  Small launches
+// also use one-wave workgroups (WPB = 1): the rows then spread over up to
+// four times as many CUs, and each CU's load pipeline serves fewer of them.
+template <typename DT, int NT, bool HOIST, int WPB>
+__global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     using C = Cvt<DT, 16>;
     constexpr int EPV = C::n;
     const uint32_t blk = xcd_block();
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t j = lane & 15u;
-    const uint32_t task = blk * 4u + wave;
+    const uint32_t task = blk * (uint32_t)WPB + wave;
     if (task >= k.rows) return;  // wave-uniform
     const bool base2 = k.base2 != 0;
     const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
@@ -371,9 +373,9 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             const int64_t blocks = (rows + RPB - 1) / RPB;
             if constexpr (V == 16 && LPR == 64 && NT > 0) {
                 if (rows <= kHoistMaxRows) {
-                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, true>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, true, 1>), dim3((uint32_t)rows), dim3(64), 0, stream, k);
                 } else {
-                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, false>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, false, 4>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
                 }
             } else {
                 hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
