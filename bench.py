@@ -275,10 +275,9 @@ class InplaceWorkload:
 class ReduceScatterWorkload:
     """Reduce-scatter flavour of the in-place merge (Kimi-K3 cached-extend
     shape): every rank's head slice of the merged output straight from all N
-    partials, with no write-back of scaled partials.  It is the out-of-place
-    combine over strided views of the partial stack: rank r's call reads
-    heads [r*Hpr, (r+1)*Hpr) of every partial; the N ranks' calls run stacked
-    along the leading R dimension, in one launch."""
+    partials, with no write-back of scaled partials.  The N ranks' slices
+    tile the heads, so their out-of-place combines run as one combine over
+    all heads of the partial stack (sim.reduce_scatter_merge)."""
 
     def __init__(self, B, dev):
         import torch

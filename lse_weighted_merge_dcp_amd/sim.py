@@ -103,20 +103,18 @@ def reduce_scatter_merge(partial: torch.Tensor, lse: torch.Tensor, out=None, out
     Rank r owns heads [r*H/N, (r+1)*H/N) and merges them from all N partials
     without writing scaled partials back: the all-reduce followed by a head
     slice in the code excerpt of cp_lse_ag_out_rs_mha (sglang PR #34213
-    report), done as a one-shot reduce-scatter.
-    The N ranks' out-of-place combines over strided views run stacked along
-    the leading R dimension in one launch.  Returns out [T, H, D] (rank r's
-    slice at heads r*H/N...) and the global LSE [T, H]."""
+    report), done as a one-shot reduce-scatter.  After that exchange rank r
+    holds its slice of every peer's partial contiguously and combines it.
+    The N ranks' slices tile the H heads, so their combines together are one
+    out-of-place combine over all heads of the stack, which reads every
+    peer's partial front to back as each rank reads its received slice.
+    Returns out [T, H, D] (rank r's slice at heads r*H/N...) and the global
+    LSE [T, H]."""
     N, T, H, D = partial.shape
     assert H % N == 0 and tuple(lse.shape) == (N, T, H)
-    assert partial.is_contiguous() and lse.is_contiguous()
-    Hpr = H // N
     if out is None:
         out = torch.empty((T, H, D), dtype=partial.dtype, device=partial.device)
     if out_lse is None:
         out_lse = torch.empty((T, H), dtype=torch.float32, device=partial.device)
-    ops.dcp_lse_combine(partial.view(N, T, N, Hpr, D).permute(2, 0, 1, 3, 4),
-                        lse.view(N, T, N, Hpr).permute(2, 0, 1, 3), is_lse_base_on_e=True,
-                        out=out.view(T, N, Hpr, D).permute(1, 0, 2, 3),
-                        out_lse=out_lse.view(T, N, Hpr).permute(1, 0, 2))
+    ops.dcp_lse_combine(partial, lse, is_lse_base_on_e=True, out=out, out_lse=out_lse)
     return out, out_lse

@@ -100,8 +100,8 @@ def test_reduce_scatter_flavour_through_strided_combine():
     scaled, ref, gr, mag = orc.inplace(inp["out"], inp["lse"], "f32", False, h0=h0, h1=h1)
     check_out(rs.cpu().numpy(), ref, mag, "f32")
     check_lse(g.cpu().numpy(), gr)
-    # all 8 ranks' slices stacked along R in one launch (the benchmarked form),
-    # with every special LSE value planted
+    # all 8 ranks' slices in one launch (the benchmarked form), with every
+    # special LSE value planted
     lse_np = inp["lse"].copy()
     lse_np[0, 0, 0] = np.nan; lse_np[3, 1, 13] = np.inf; lse_np[:, 2, 30] = -np.inf; lse_np[5, 4, 95] = -np.inf
     out, g = sim.reduce_scatter_merge(part, torch.from_numpy(lse_np).to(DEV))
@@ -113,7 +113,7 @@ def test_reduce_scatter_flavour_through_strided_combine():
 def test_inplace_full_size_sampled():
     """8 x [16384, 96, 512] fp32 partials (24 GiB) merged in one call, in the
     launch configurations the benchmark times: first the reduce-scatter
-    flavour (every rank's head slice, stacked; the partials must stay
+    flavour (every rank's head slice, in one launch; the partials must stay
     untouched), then in place; 3000 sampled (t, h) rows are checked (scaled
     partials of all ranks, merged row, G) for both."""
     w = synth.WORKLOADS["kimi"]
