@@ -65,6 +65,29 @@ def kernel_source_hash() -> str:
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
+def algorithmic_bytes(key, B=None):
+    """Bytes each kernel of a workload must move per launch (what the method
+    itself reads and writes; no re-reads):
+      pack     2 N B H (D e + 4)     every rank reads and writes its rows
+      combine  (N + 1) B H (D e + 4) N partial rows read, out + G written
+      inplace  T H (N (4D + 4) + N 4D + 4D + 4)
+      kimi-rs combine  T H (N (4D + 4) + 4D + 4)."""
+    from lse_weighted_merge_dcp_amd import synth
+
+    w = synth.WORKLOADS["kimi" if key == "kimi-rs" else key]
+    if B is not None:
+        w = w.with_batch(B)
+    if key == "kimi":
+        row = 4 * w.D
+        return {"inplace": w.B * w.H * (w.N * (row + 4) + w.N * row + row + 4)}
+    if key == "kimi-rs":
+        row = 4 * w.D
+        return {"combine": w.B * w.H * (w.N * (row + 4) + row + 4)}
+    row = w.D * w.esize + 4
+    per_th = w.B * w.H
+    return {"pack": 2 * w.N * per_th * row, "combine": (w.N + 1) * per_th * row}
+
+
 class A2AWorkload:
     """Interleaved or split pack + combine, `layers` distinct buffer sets."""
 
@@ -110,11 +133,8 @@ class A2AWorkload:
                 self.stk[l].pack(self.src[l], self.lse[l])
                 self.stk[l].exchange()
         torch.cuda.synchronize()
-        e = w.esize
-        row = w.D * e + 4
-        per_th = w.B * w.H
-        self.bytes_pack = 2 * w.N * per_th * row            # every rank reads and writes its B*H rows
-        self.bytes_combine = w.N * per_th * row + per_th * row   # read N partials per output row, write out + G
+        nb = algorithmic_bytes(key, B)
+        self.bytes_pack, self.bytes_combine = nb["pack"], nb["combine"]
         self.bytes_layer = self.bytes_pack + self.bytes_combine
         self.dtype = w.dtype
 
@@ -227,8 +247,7 @@ class InplaceWorkload:
         self.glse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
-        row = 4 * w.D
-        self.bytes_call = w.B * w.H * (w.N * (row + 4) + w.N * row + row + 4)
+        self.bytes_call = algorithmic_bytes("kimi", B)["inplace"]
         self.dtype = "f32"
 
     def run(self):
@@ -296,8 +315,7 @@ class ReduceScatterWorkload:
         self.glse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
-        row = 4 * w.D
-        self.bytes_call = w.B * w.H * (w.N * (row + 4) + row + 4)
+        self.bytes_call = algorithmic_bytes("kimi-rs", B)["combine"]
         self.dtype = "f32"
 
     def run(self):
@@ -634,10 +652,58 @@ def summarize_counters(directory, workload):
             continue
         out["kernels"][kname] = {"FETCH_SIZE": f, "WRITE_SIZE": wv, "read_bytes": f * fs, "write_bytes": wv * ws,
                                  "hbm_bytes_per_launch": f * fs + wv * ws}
+    alg = algorithmic_bytes(workload)
+    for kname, v in out["kernels"].items():
+        v["algorithmic_bytes_per_launch"] = alg.get(kname)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "counters_%s.json" % workload), "w") as fo:
         json.dump(out, fo, indent=1)
+    with open(os.path.join(ROOT, "profiles", "counters_%s.md" % workload), "w") as fo:
+        fo.write(counters_markdown(out, directory))
     print(json.dumps(out, indent=1))
+
+
+def counters_markdown(d, directory):
+    w = d["workload"]
+    dirs = directory.split(",")
+    c = d["copy_reference"]
+    lines = [
+        "# HBM traffic counters: %s workload" % w,
+        "",
+        "Kernel source hash `%s` (`counters_%s.json`; bench.py reports these bytes as" % (d["kernel_source"], w),
+        "`roofline.traffic` only while the kernel sources still hash to it).  Two rocprofv3",
+        "counter runs of the same short program (`bench.py --counter-run`: a 1 GiB",
+        "`torch.neg` pass as the scale reference, then three launches of each kernel on",
+        "the workload's buffers), then the summary:",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/%s -o run -- python3 $REPO/bench.py --workload %s --counter-run"
+        % (dirs[0], w),
+        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/%s -o run -- python3 $REPO/bench.py --workload %s --counter-run"
+        % (dirs[-1], w),
+        "python3 bench.py --workload %s --summarize-counters %s" % (w, directory),
+        "```",
+        "",
+        "Scale reference: `torch.neg` over 2^28 fp32 reads and writes exactly 1 GiB; it",
+        "reads FETCH_SIZE = %.0f and WRITE_SIZE = %.0f per dispatch, so one FETCH_SIZE" % (c["FETCH_SIZE"], c["WRITE_SIZE"]),
+        "unit is %.0f bytes and one WRITE_SIZE unit %.0f bytes on this part." % (c["fetch_scale"], c["write_scale"]),
+        "",
+        "| Kernel | FETCH_SIZE | WRITE_SIZE | HBM read | HBM write | HBM total | Algorithmic | Ratio |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for k, v in d["kernels"].items():
+        a = v.get("algorithmic_bytes_per_launch")
+        lines.append("| %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            k, "{:,.0f}".format(v["FETCH_SIZE"]), "{:,.0f}".format(v["WRITE_SIZE"]), _fmt_bytes(v["read_bytes"]),
+            _fmt_bytes(v["write_bytes"]), _fmt_bytes(v["hbm_bytes_per_launch"]), _fmt_bytes(a) if a else "-",
+            "%.3f" % (v["hbm_bytes_per_launch"] / a) if a else "-"))
+    lines.append("")
+    return "\n".join(lines)
+
+
+def _fmt_bytes(x):
+    return "%.2f GB" % (x / 1e9) if x >= 1e9 else "%.2f MB" % (x / 1e6)
 
 
 if __name__ == "__main__":
