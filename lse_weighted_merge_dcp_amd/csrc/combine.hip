@@ -109,8 +109,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 
     if constexpr (NT > 0) {
         // ---- fixed N <= 16: lane j of every DPP row holds peer j ----------
+        // The payload loads go out right after the LSE load, so the LSE
+        // reduction overlaps them (one memory round trip per wave); lanes
+        // past the row end read its last chunk again and never store it.
         float lj = -INFINITY;
         if (j < (uint32_t)NT) lj = load_f32(lbase + (int64_t)j * k.rl_N);
+        const uint32_t c = seg * LPR + li;
+        const bool on = c < k.chunks;
+        const int64_t coff = (int64_t)(on ? c : k.chunks - 1u) * V;
+        Vec<V> x[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) x[i] = vload_stream<V>(rbase + i * k.r_N + coff);
         LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj), base2);
         float w = 0.0f;
         if (st.live) {
@@ -123,40 +132,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
         [&]<int... I>(std::integer_sequence<int, I...>) { ((wi[I] = row_bcast<I>(w)), ...); }
         (std::make_integer_sequence<int, NT>{});
 
-        {
-            const uint32_t c = seg * LPR + li;
-            if (c < k.chunks) {
-                const int64_t coff = (int64_t)c * V;
-                Vec<V> x[NT];
+        float acc[EPV];
 #pragma unroll
-                for (int i = 0; i < NT; ++i) x[i] = vload<V>(rbase + i * k.r_N + coff);
-                float acc[EPV];
+        for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+        for (int i = 0; i < NT; ++i) {
+            float f[EPV];
+            C::unpack(x[i], f);
 #pragma unroll
-                for (int i = 0; i < NT; ++i) {
-                    float f[EPV];
-                    C::unpack(x[i], f);
+            for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], f[e], acc[e]);
+        }
+        bool bad = false;
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], f[e], acc[e]);
-                }
-                bool bad = false;
+        for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+            // a non-finite payload value: re-form the sum with the guards
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) bad |= !finite_f(acc[e]);
-                if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+            for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
+            for (int i = 0; i < NT; ++i) {
+                float f[EPV];
+                C::unpack(vload<V>(rbase + i * k.r_N + coff), f);
 #pragma unroll
-                    for (int i = 0; i < NT; ++i) {
-                        float f[EPV];
-                        C::unpack(x[i], f);
-#pragma unroll
-                        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
-                    }
-                }
-                vstore<V>(obase + coff, C::pack(acc));
+                for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
             }
         }
+        if (on) vstore<V>(obase + coff, C::pack(acc));
         if (k.olse != nullptr && li == 0 && seg == 0)
             *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
     } else {

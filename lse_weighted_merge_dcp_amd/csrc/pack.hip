@@ -37,7 +37,6 @@ struct PackK {
     FastDiv f_steps, f_H, f_B, f_Hpr;
 };
 
-constexpr int kPackU = 4;
 constexpr uint32_t kNegInfBits = 0xff800000u;   // -inf as an fp32 word
 
 template <int V, int LPR, int U>
@@ -249,9 +248,9 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
     return hipSuccess;
 }
 
-template <int V, int LPR>
-hipError_t run(const PackArgs& a, hipStream_t stream) {
-    constexpr int64_t RPB = 4 * (64 / LPR) * kPackU;
+template <int V, int LPR, int U>
+hipError_t run_u(const PackArgs& a, hipStream_t stream) {
+    constexpr int64_t RPB = 4 * (64 / LPR) * U;
     const int64_t chunks = a.dst ? a.row_bytes / V : 1;
     const int64_t steps = (chunks + LPR - 1) / LPR;
     const int64_t per_r = a.B * a.H * steps;
@@ -291,12 +290,25 @@ hipError_t run(const PackArgs& a, hipStream_t stream) {
             k.f_B = make_fastdiv(k.B);
             k.f_Hpr = make_fastdiv(k.Hpr);
             const int64_t blocks = (vrows + RPB - 1) / RPB;
-            hipLaunchKernelGGL((pack_kernel<V, LPR, kPackU>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+            hipLaunchKernelGGL((pack_kernel<V, LPR, U>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }
     return hipSuccess;
+}
+// Rows per wave: four when that still leaves at least 512 workgroups, else
+// fewer, so small launches spread over more CUs (measured on MI355X: the
+// split-layout pack of one rank 5.4 -> 4.5 us with two, the smallest
+// interleaved pack 3.4 -> 2.1 us with one).
+template <int V, int LPR>
+hipError_t run(const PackArgs& a, hipStream_t stream) {
+    const int64_t chunks = a.dst ? a.row_bytes / V : 1;
+    const int64_t vrows = a.R * a.B * a.H * ((chunks + LPR - 1) / LPR);
+    const int64_t per_block = 4 * (64 / LPR);   // rows per workgroup and unit of U
+    if (vrows >= 512 * per_block * 4) return run_u<V, LPR, 4>(a, stream);
+    if (vrows >= 512 * per_block * 2) return run_u<V, LPR, 2>(a, stream);
+    return run_u<V, LPR, 1>(a, stream);
 }
 
 template <int V>
