@@ -178,3 +178,16 @@ def test_fastdiv_matches_integer_division(tmp_path):
     subprocess.check_call(["g++", "-O2", "-std=c++17", "-I" + CSRC, str(src), "-o", exe])
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout
+
+
+def test_header_compiles_as_c_and_the_c_client_links(tmp_path):
+    """include/dcpmerge.h is plain C: a C11 caller (tests/c_abi_client.c)
+    compiles with -Wall -Wextra -Werror and links against libdcpmerge.so and
+    the HIP runtime.  Run without arguments it prints its usage and exits
+    before any HIP call."""
+    import __graft_entry__
+
+    _lib.lib()
+    exe = __graft_entry__.build_c_client(str(tmp_path / "client"))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
