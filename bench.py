@@ -17,7 +17,7 @@ bytes (what the method must move: (3N+1)(D*e+4) bytes per (token, head) for
 pack + combine), microseconds per layer, the roofline entry of the dominant
 kernel (per-launch duration from HIP events on the launch stream, over a
 replayed graph of that kernel's launches) and the CPU oracle timed on a
-bounded sample.  Beside them: the p10/p50/p90 step time, the rate of a plain
+bounded sample, on every host thread and on one.  Beside them: the p10/p50/p90 step time, the rate of a plain
 2 GiB device-to-device copy measured in the same run (the practical ceiling),
 and for the pack + combine workloads the per-rank share (one rank's pack and
 one destination's combine at their real shapes) and the cache-resident step
@@ -546,7 +546,16 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
+        # the oracle on every host thread, then on one (a shorter sample)
+        from oracle import oracle as orc
+
         cpu = wl.cpu_sample(args.cpu_budget)
+        n_all = orc.num_threads()
+        orc.set_num_threads(1)
+        one = wl.cpu_sample(max(1.0, args.cpu_budget / 3))
+        orc.set_num_threads(n_all)
+        cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": one["cores"],
+                              "sample": one["sample"]}
 
     res = {
         "metric": METRIC,

@@ -190,6 +190,15 @@ ORC_API void orc_inplace(const double* o, const double* l, int64_t N, int64_t P,
     }
 }
 
+/* Threads the parallel loops use from now on (n >= 1); for timing only. */
+ORC_API void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Thread count OpenMP will use (reported with the CPU baseline). */
 ORC_API int orc_num_threads(void) {
 #ifdef _OPENMP

@@ -68,6 +68,8 @@ def load_library(path: str):
     lib.orc_inplace.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = c_int
+    lib.orc_set_num_threads.argtypes = [c_int]
+    lib.orc_set_num_threads.restype = None
     return lib
 
 
@@ -83,6 +85,12 @@ def _load(lib=None):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; results do not
+    depend on it: every loop iteration is an independent row)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray) -> int:
