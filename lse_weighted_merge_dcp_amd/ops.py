@@ -53,7 +53,9 @@ def _on_gpu(*ts: Optional[torch.Tensor]) -> None:
 
 def _payload_ok(t: torch.Tensor, name: str) -> None:
     _require(t.dtype in _DTYPE, "%s: unsupported dtype %s" % (name, t.dtype))
-    _require(t.shape[-1] == 1 or t.stride(-1) == 1, "%s: the last (D) dimension must be contiguous" % name)
+    # (an empty tensor's strides are arbitrary; the call is then a no-op)
+    _require(t.numel() == 0 or t.shape[-1] == 1 or t.stride(-1) == 1,
+             "%s: the last (D) dimension must be contiguous" % name)
 
 
 def _lse_ok(t: torch.Tensor, name: str) -> None:
@@ -77,6 +79,9 @@ def interleaved_views(send: torch.Tensor, D: int) -> Tuple[torch.Tensor, torch.T
     _require(D % lpd == 0, "D (%d) must be a multiple of the LSE pack dim (%d)" % (D, lpd))
     _require(send.shape[-1] == D + lpd, "send rows must hold D + lpd = %d elements" % (D + lpd))
     _require(send.is_contiguous(), "send buffer must be contiguous")
+    if send.numel() == 0:
+        # nothing to address; an empty tensor's strides may not allow the view
+        send = torch.empty(send.shape, dtype=send.dtype, device=send.device)
     words = send.view(torch.float32)
     return send[..., :D], words[..., D // lpd]
 

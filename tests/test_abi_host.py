@@ -142,6 +142,11 @@ def test_binding_rejects_host_tensors_and_bad_layouts():
     assert words.stride() == (2 * 4 * 33, 4 * 33, 33)
     with pytest.raises(ValueError):
         ops.interleaved_views(torch.zeros(2, 2, 4, 65, dtype=torch.bfloat16), 63)
+    # empty buffers: any strides (numpy gives zero-size arrays zero strides)
+    import numpy as np
+    empty = torch.from_numpy(np.zeros((2, 0, 4, 66), np.float16))
+    pay, words = ops.interleaved_views(empty, 64)
+    assert pay.shape == (2, 0, 4, 64) and words.shape == (2, 0, 4)
 
 
 FASTDIV_TEST = r"""
