@@ -1,0 +1,44 @@
+"""bench.py on the host (no GPU): the one-GPU guard and the algorithmic byte
+counts behind every GB/s figure it prints."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_more_than_one_gpu_exits_with_a_message(argv, env):
+    e = dict(os.environ)
+    e.update(env)
+    r = subprocess.run([sys.executable, BENCH] + argv, capture_output=True, text=True, timeout=120, env=e)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_bytes_per_layer():
+    """Per-layer bytes of the pack + combine path, (3N + 1)(D e + 4) per
+    (token, head), and of the in-place and reduce-scatter merges."""
+    b = bench.algorithmic_bytes("dsv3")
+    assert b["pack"] + b["combine"] == 64 * 128 * (3 * 8 + 1) * (512 * 2 + 4) == 210_534_400
+    assert b["pack"] == 134_742_016 and b["combine"] == 75_792_384
+    for B, total in [(1, 6_447_616), (8, 51_580_928), (64, 412_647_424), (256, 1_650_589_696), (512, 3_301_179_392)]:
+        b = bench.algorithmic_bytes("longctx", B)
+        assert b["pack"] + b["combine"] == total == B * 128 * (3 * 16 + 1) * 1028
+    assert bench.algorithmic_bytes("tiny")["pack"] + bench.algorithmic_bytes("tiny")["combine"] == 58_240
+    split = bench.algorithmic_bytes("split")
+    assert split["pack"] + split["combine"] == 256 * 64 * (3 * 4 + 1) * (128 * 2 + 4) == 55_377_920
+    # in place: read N rows of 4D + 4, write N rows of 4D back and the merged row + G
+    assert bench.algorithmic_bytes("kimi")["inplace"] == 16384 * 96 * 34_852 == 54_817_456_128
+    # reduce-scatter flavour: no write-back
+    assert bench.algorithmic_bytes("kimi-rs")["combine"] == 16384 * 96 * (8 * 2052 + 2052) == 29_047_652_352
+
+
+def test_percentiles():
+    p = bench.percentiles([5.0, 1.0, 3.0, 2.0, 4.0, 6.0, 7.0, 8.0, 9.0, 10.0, 11.0])
+    assert p == {"p10": 2.0, "p50": 6.0, "p90": 10.0}
