@@ -136,7 +136,10 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
  * order, no atomics.
  *
  * recv_o may be any strided view [R, N, B, Hpr, D] (e.g. the permuted views of
- * the split layout, or one destination's slice of a stacked send buffer);
+ * the split layout, or one destination's slice of a stacked send buffer).
+ * Over the head slice [h0, h1) of an [N, T, H, D] partial stack (B = T,
+ * Hpr = h1 - h0) it is the reduce-scatter flavour of dcp_lse_combine_inplace:
+ * the same out and out_lse, with the partials left untouched;
  * strides (ro_R, ro_N, ro_B, ro_H) elements; recv_lse (rl_R, rl_N, rl_B, rl_H)
  * words; out (oo_R, oo_B, oo_H) elements; out_lse (ol_R, ol_B, ol_H) words.
  * Errors: DCP_ERR_NULL, _SHAPE, _DTYPE, _LSE_BASE, _STRIDE, _ALIGN, _LAUNCH.
