@@ -25,6 +25,9 @@
  *     to 4 bytes.  Faster kernels are chosen when the payload rows are
  *     4-byte aligned and D * element size is a multiple of 16 bytes.
  *   - Outputs must not overlap inputs (except where stated) or each other.
+ *     Stated exception: the out of dcp_unpack_combine may exactly alias
+ *     recv_o's peer 0 rows (same address and strides), merging in place into
+ *     the first received partial; out_lse must never alias recv_lse.
  *   - Errors are detected on the host before anything is enqueued: on any
  *     error nothing is written.  A zero-sized call (R, B or T = 0) is DCP_OK.
  *   - Size limits: the heads of one token (H, or Hpr for the combine) times

@@ -187,6 +187,38 @@ def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
     check_lse(gg.cpu().numpy(), gr)
 
 
+@pytest.mark.parametrize("dt,N,B,Hpr,D", [
+    ("bf16", 8, 5, 4, 512),      # row-per-wave kernel, latency order
+    ("bf16", 8, 160, 16, 512),   # row-per-wave kernel, bandwidth order (2560 rows)
+    ("f32", 4, 6, 3, 1000),      # several segments per row
+    ("f16", 4, 9, 5, 128),       # short-row kernel
+    ("f32", 17, 4, 3, 64),       # any-N path
+    ("bf16", 3, 4, 2, 100),      # element-granular rows
+    ("f32", 1, 4, 3, 64),        # N = 1 copy onto itself
+])
+def test_out_may_alias_peer_zero(dt, N, B, Hpr, D):
+    """out may be exactly recv_o's peer 0 rows: the merge lands in place in
+    the first received partial, and matches the oracle on the original input."""
+    say("alias", dt, N, B, Hpr, D)
+    g = torch.Generator().manual_seed(N * 31 + D)
+    o = synth.to_storage(torch.randn(N, B, Hpr, D, generator=g), dt)
+    lse = np.random.default_rng(D + N).normal(0, 3, size=(N, B, Hpr)).astype(np.float32)
+    lse[:, 0, 0] = -np.inf
+    d_o = to_dev(o, dt, DEV)
+    d_l = torch.from_numpy(lse).to(DEV)
+    out, gg = ops.dcp_lse_combine(d_o, d_l, is_lse_base_on_e=True, out=d_o[0])
+    assert out.data_ptr() == d_o.data_ptr()
+    got = to_host(d_o[0], dt)
+    if N == 1:
+        assert np.array_equal(got.view(np.uint8), o[0].view(np.uint8))
+        return
+    ref, gr, mag, _ = orc.combine(o, lse, dt, False)
+    check_out(decode(got, dt), ref, mag, dt)
+    check_lse(gg.cpu().numpy(), gr)
+    # the other peers' rows are untouched
+    assert np.array_equal(to_host(d_o[1:], dt).view(np.uint8), o[1:].view(np.uint8))
+
+
 def test_single_rank_identity_keeps_nan_and_inf_bits():
     o = np.random.default_rng(0).normal(size=(1, 3, 2, 64)).astype(np.float32)
     o[0, 0, 0, :3] = [np.nan, np.inf, -np.inf]
