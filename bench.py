@@ -453,7 +453,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build simulates all DCP ranks on a single MI355X "
+        print("bench.py measures one GPU only: it simulates all DCP ranks on a single MI355X "
               "(stacked in its HBM) and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
