@@ -567,6 +567,9 @@ def main():
         cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": one["cores"],
                               "sample": one["sample"]}
 
+    props = torch.cuda.get_device_properties(dev)
+    device = {"arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+              "memory_bytes": props.total_memory}
     res = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -594,6 +597,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "kernel_source": kernel_source_hash(),
+        "device": device,
     }
     print(json.dumps(res), flush=True)
 
