@@ -130,9 +130,13 @@ struct StreamK {
 // on the DeepSeek-V3-shaped pack and up to 20% on small launches, where more
 // waves spread the same bytes over more CUs.
 constexpr int kStreamU = 1;
+// Launches of at least this many wave-steps use 8-wave workgroups, smaller
+// ones 4-wave workgroups (measured: 1.5-2% faster on large launches, 1-3%
+// slower on small ones).
+constexpr int64_t kStreamWide = 32768;
 
-template <int U>
-__global__ __launch_bounds__(256) void pack_stream_kernel(const StreamK k) {
+template <int U, int WPB>
+__global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     Vec<16> v[U];
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void pack_stream_kernel(const StreamK k) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         on[u] = false;
-        const uint32_t ws = (blockIdx.x * (uint32_t)U + (uint32_t)u) * 4u + wave;  // wave-uniform
+        const uint32_t ws = (blockIdx.x * (uint32_t)U + (uint32_t)u) * (uint32_t)WPB + wave;  // wave-uniform
         if (ws < k.nsteps) {
             const uint32_t blk = fdiv(ws, k.f_S);       // blocks ordered (r, b, p): sequential source reads
             const uint32_t s = ws - blk * k.S;
@@ -239,8 +243,13 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.f_N = make_fastdiv(k.N);
             k.f_B = make_fastdiv(k.B);
             k.f_Wd = make_fastdiv(k.Wd);
-            const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-            hipLaunchKernelGGL((pack_stream_kernel<kStreamU>), dim3(blocks), dim3(256), 0, stream, k);
+            if (k.nsteps >= kStreamWide) {
+                const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
+                hipLaunchKernelGGL((pack_stream_kernel<kStreamU, 8>), dim3(blocks), dim3(512), 0, stream, k);
+            } else {
+                const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
+                hipLaunchKernelGGL((pack_stream_kernel<kStreamU, 4>), dim3(blocks), dim3(256), 0, stream, k);
+            }
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
