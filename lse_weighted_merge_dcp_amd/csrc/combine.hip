@@ -372,16 +372,15 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             k.f_steps = make_fastdiv(k.steps);
             k.base2 = a.base2 ? 1 : 0;
             const int64_t blocks = (rows + RPB - 1) / RPB;
+            hipError_t e;
             if constexpr (V == 16 && LPR == 64 && NT > 0) {
-                if (rows <= kHoistMaxRows) {
-                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, true, 1>), dim3((uint32_t)rows), dim3(64), 0, stream, k);
-                } else {
-                    hipLaunchKernelGGL((combine_wave_kernel<DT, NT, false, 4>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
-                }
+                if (rows <= kHoistMaxRows)
+                    e = launch_kernel(combine_wave_kernel<DT, NT, true, 1>, dim3((uint32_t)rows), dim3(64), stream, k);
+                else
+                    e = launch_kernel(combine_wave_kernel<DT, NT, false, 4>, dim3((uint32_t)blocks), dim3(256), stream, k);
             } else {
-                hipLaunchKernelGGL((combine_kernel<DT, V, LPR, NT>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
+                e = launch_kernel(combine_kernel<DT, V, LPR, NT>, dim3((uint32_t)blocks), dim3(256), stream, k);
             }
-            hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }

@@ -62,6 +62,15 @@ struct InplaceArgs {
     bool base2;
 };
 
+// Launch kernel(arg) and return that launch's own status.  (Reading the
+// thread's last error after a launch would also report, and clear, a stale
+// error the caller left from an unrelated call.)
+template <typename Arg>
+inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream, const Arg& arg) {
+    void* args[] = {const_cast<Arg*>(&arg)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+}
+
 // Each launcher returns hipSuccess or the launch error; arguments are
 // assumed validated by the caller.
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);

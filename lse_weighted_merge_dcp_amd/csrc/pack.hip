@@ -243,14 +243,14 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.f_N = make_fastdiv(k.N);
             k.f_B = make_fastdiv(k.B);
             k.f_Wd = make_fastdiv(k.Wd);
+            hipError_t e;
             if (k.nsteps >= kStreamWide) {
                 const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
-                hipLaunchKernelGGL((pack_stream_kernel<kStreamU, 8>), dim3(blocks), dim3(512), 0, stream, k);
+                e = launch_kernel(pack_stream_kernel<kStreamU, 8>, dim3(blocks), dim3(512), stream, k);
             } else {
                 const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-                hipLaunchKernelGGL((pack_stream_kernel<kStreamU, 4>), dim3(blocks), dim3(256), 0, stream, k);
+                e = launch_kernel(pack_stream_kernel<kStreamU, 4>, dim3(blocks), dim3(256), stream, k);
             }
-            hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }
@@ -299,8 +299,7 @@ hipError_t run_u(const PackArgs& a, hipStream_t stream) {
             k.f_B = make_fastdiv(k.B);
             k.f_Hpr = make_fastdiv(k.Hpr);
             const int64_t blocks = (vrows + RPB - 1) / RPB;
-            hipLaunchKernelGGL((pack_kernel<V, LPR, U>), dim3((uint32_t)blocks), dim3(256), 0, stream, k);
-            hipError_t e = hipGetLastError();
+            const hipError_t e = launch_kernel(pack_kernel<V, LPR, U>, dim3((uint32_t)blocks), dim3(256), stream, k);
             if (e != hipSuccess) return e;
         }
     }
