@@ -25,7 +25,8 @@ DEV = torch.device("cuda:0")
 
 
 @pytest.mark.parametrize("dt,N,B,Hpr,D,layout", [
-    ("bf16", 8, 9, 16, 512, "interleaved"),   # stream kernel
+    ("bf16", 8, 9, 16, 512, "interleaved"),   # stream kernel, 4-wave workgroups
+    ("bf16", 16, 40, 8, 512, "interleaved"),  # stream kernel, 8-wave workgroups (>= 32768 wave-steps)
     ("f32", 2, 7, 4, 64, "interleaved"),      # row kernel (short rows)
     ("f16", 4, 6, 16, 128, "split"),          # split layout
 ])
