@@ -55,10 +55,15 @@ CSRC = os.path.join(ROOT, "lse_weighted_merge_dcp_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library's sources with comments and blank lines removed:
+    it changes when the code changes, not when a comment does."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp"))
                     + glob.glob(os.path.join(CSRC, "*.cpp"))):
-        h.update(open(p, "rb").read())
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(line.rstrip() for line in text.splitlines() if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

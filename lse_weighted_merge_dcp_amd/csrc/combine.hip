@@ -5,20 +5,23 @@
 // Per output row (r, b, hl):  G = log_beta sum_i beta^l_i,
 // w_i = nan_to_num(beta^(l_i - G)),  out = sum_i w_i * nan_to_num(o_i).
 //
-// Work mapping.  One row group of LPR lanes (16, 32 or 64) owns one segment
+// Work mapping.  One row group of LPR lanes (16 or 64) owns one segment
 // (LPR x vector bytes) of one output row; rows longer than that are split
 // over several groups, each redoing the (tiny) LSE reduction, so no wave
-// ever waits on its own stores before loading again.  Inside a group, every 16-lane DPP row redundantly derives G and the
-// weights: lane j loads l_j, the maximum, the special-value flags and the
-// sum of beta^(l_j - m) are reduced with row_ror DPP steps, and each lane's
-// w_j = beta^(l_j - m) / sum is broadcast to the row with row_newbcast.  The
-// payload is then streamed in 16-byte vectors: every lane loads its chunk of
-// all N peers (N loads in flight), and accumulates w_i * o_i in fp32.
+// ever waits on its own stores before loading again.  Inside a group, every
+// 16-lane DPP row redundantly derives G and the weights: lane j loads l_j,
+// the maximum, the special-value flags and the sum of beta^(l_j - m) are
+// reduced with row_ror DPP steps, and each lane's w_j = beta^(l_j - m) / sum
+// is broadcast to the row with row_newbcast.  The payload moves in 16-byte
+// vectors: every lane loads its chunk of all N peers (N loads in flight) and
+// accumulates w_i * o_i in fp32.  Where it pays (short rows, small launches)
+// the payload loads go out right after the LSE load, so the reduction
+// overlaps them; large launches of long rows load after the weights.
 //
 // Guards cost nothing on clean data: the sum is formed from the raw values
 // and checked once per output element.  A finite sum proves every term was
 // finite, i.e. nan_to_num would have changed nothing; otherwise the wave
-// re-forms the sum from the guarded values still held in registers.
+// reads its rows again and re-forms the sum from the guarded values.
 //
 // N > 16 (or N not in {2,4,8,16}) takes the general path: lane j handles
 // peers j, j+16, ..., and each lane recomputes the weight of each peer as it
