@@ -1,0 +1,51 @@
+"""Calls keep no state and enqueue only on the caller's stream: two
+independent decode layers issued concurrently on two streams give, bit for
+bit, what they give one after the other on one stream."""
+import pytest
+import torch
+
+from lse_weighted_merge_dcp_amd import sim, synth
+
+from helpers import say, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def layer_inputs(key, B, shift):
+    w = synth.WORKLOADS[key].with_batch(B)
+    inp = synth.rank_inputs(w)
+    src = to_dev(inp["out"], w.dtype, DEV)
+    lse = torch.from_numpy(inp["lse"]).to(DEV) + shift
+    st = sim.StackedInterleaved(w.N, w.B, w.H, w.D, src.dtype, DEV)
+    out = torch.empty((w.N, w.B, w.Hpr, w.D), dtype=src.dtype, device=DEV)
+    g = torch.empty((w.N, w.B, w.Hpr), dtype=torch.float32, device=DEV)
+    return w, src, lse, st, out, g
+
+
+def run_layer(w, src, lse, st, out, g):
+    st.pack(src, lse)
+    st.combine(is_lse_base_on_e=not w.base2, out=out, out_lse=g)
+
+
+def test_concurrent_streams_match_sequential():
+    say("two streams")
+    a = layer_inputs("longctx", 64, 0.0)
+    b = layer_inputs("longctx", 8, 1.5)
+    run_layer(*a)
+    run_layer(*b)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (a[3].send, a[4], a[5], b[3].send, b[4], b[5])]
+    for t in (a[3].send, a[4], a[5], b[3].send, b[4], b[5]):
+        t.zero_()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            run_layer(*a)
+        with torch.cuda.stream(s2):
+            run_layer(*b)
+        torch.cuda.synchronize()
+        got = [a[3].send, a[4], a[5], b[3].send, b[4], b[5]]
+        for x, y in zip(got, ref):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), "concurrent run %d differs" % rep
