@@ -176,10 +176,14 @@ class A2AWorkload:
         return fns
 
     def step_launches(self):
+        return [f for _, f in self.named_step()]
+
+    def named_step(self):
+        """The step's calls in order, each with the kernel it launches."""
         fns = []
         for l in range(self.layers):
-            fns.append(lambda l=l: self.pack(l))
-            fns.append(lambda l=l: self.combine(l))
+            fns.append(("pack", lambda l=l: self.pack(l)))
+            fns.append(("combine", lambda l=l: self.combine(l)))
         return fns
 
     def kernels(self):
@@ -266,6 +270,9 @@ class InplaceWorkload:
     def kernels(self):
         return [("inplace", self.bytes_call, [self.run])]
 
+    def named_step(self):
+        return [("inplace", self.run)]
+
     def step_bytes(self):
         return self.bytes_call
 
@@ -330,6 +337,9 @@ class ReduceScatterWorkload:
 
     def kernels(self):
         return [("combine", self.bytes_call, [self.run])]
+
+    def named_step(self):
+        return [("combine", self.run)]
 
     def step_bytes(self):
         return self.bytes_call
@@ -439,6 +449,71 @@ def per_launch_us(launches, reps, restore=None, min_replay_us=1000.0):
     return us, g
 
 
+def _sleep_cycles_per_ms():
+    import torch
+
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(1_000_000)
+    b.record()
+    b.synchronize()
+    return 1_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def in_step_us(named, reps, restore=None):
+    """Average device time of each kernel inside the step.
+
+    The step's calls are issued eagerly, in the step's order, behind a
+    GPU-side wait (torch.cuda._sleep) that outlasts the host's enqueueing,
+    so that the device runs them back to back as it runs the step graph.
+    The launches of one kernel per replay carry timing events on their own
+    dispatches (ops.time_next_call), so no marker packet sits between the
+    kernels; the replays take the kernels in turn.  `named` is the step as
+    (kernel name, call) pairs.  Returns ({name: us per launch}, {name:
+    median device span in ms of the replays that timed it, from its first
+    timed start to its last timed end})."""
+    import torch
+
+    from lse_weighted_merge_dcp_amd import ops, timing
+
+    order = []
+    for n, _ in named:
+        if n not in order:
+            order.append(n)
+    if restore:
+        restore()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _, f in named:
+        f()
+    enqueue_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    sleep = getattr(torch.cuda, "_sleep", None)
+    gate = int(_sleep_cycles_per_ms() * (5.0 + 4.0 * enqueue_ms)) if sleep else 0
+    events = [(timing.Event(), timing.Event()) for _ in named]
+    total = {n: 0.0 for n in order}
+    count = {n: 0 for n in order}
+    spans = {n: [] for n in order}
+    for r in range(reps * len(order)):
+        name = order[r % len(order)]
+        if restore:
+            restore()
+        if gate:
+            sleep(gate)
+        timed = [i for i, (n, _) in enumerate(named) if n == name]
+        for i, (n, f) in enumerate(named):
+            if n == name:
+                ops.time_next_call(*events[i])
+            f()
+        torch.cuda.synchronize()
+        for i in timed:
+            total[name] += events[i][0].elapsed_us(events[i][1])
+            count[name] += 1
+        spans[name].append(events[timed[0]][0].elapsed_us(events[timed[-1]][1]) / 1e3)
+    return {n: total[n] / count[n] for n in order}, {n: round(percentiles(v)["p50"], 4) for n, v in spans.items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,11 +610,17 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     gbs = wl.step_bytes() / (wall / args.steps) / 1e9
 
-    # ---- per-kernel durations: HIP events around replayed graphs of one kernel
+    # ---- per-kernel durations: inside the step (events on the kernels' own
+    # dispatches), and cold (HIP events around a replayed graph of that
+    # kernel's launches back to back)
+    reps = max(3, args.steps // 4)
+    in_step, spans = in_step_us(wl.named_step(), reps, restore=restore)
     kinfo = {}
     for name, nbytes, launches in wl.kernels():
-        us, _ = per_launch_us(launches, reps=max(3, args.steps // 4), restore=restore)
-        kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9}
+        cold, _ = per_launch_us(launches, reps=reps, restore=restore)
+        us = in_step[name]
+        kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                       "cold_us_per_launch": cold, "cold_GBps": nbytes / (cold * 1e-6) / 1e9}
     extra = {}
     layers = getattr(wl, "layers", 1)
     if hasattr(wl, "per_rank"):
@@ -599,7 +680,12 @@ def main():
                     for k, v in kinfo.items()},
         **extra,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "timing": "inside the step: events on the kernel's own dispatches in eager replays of "
+                               "the step (one kernel timed per replay)",
+                     "cold_achieved": round(kinfo[dom]["cold_GBps"], 1),
+                     "cold_frac": round(kinfo[dom]["cold_GBps"] / PEAK_HBM_GBS, 4)},
+        "timed_replay_span_ms": spans,
         "cpu_baseline": cpu,
         "kernel_source": kernel_source_hash(),
         "device": device,

@@ -40,7 +40,35 @@ bool shape_fits(int64_t H, int64_t row_bytes) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DCP_OK : DCP_ERR_LAUNCH; }
 
+// The timing request of dcp_time_next_call waits in `armed` until the next
+// compute entry point takes it; that call holds it in `active` while it runs.
+thread_local dcp::CallTiming armed;
+thread_local dcp::CallTiming active;
+
+// Gives the armed request (if any) to the running call, and clears both when
+// the call returns, whatever its status.
+struct TimedCall {
+    TimedCall() {
+        active = armed;
+        armed = dcp::CallTiming{};
+    }
+    ~TimedCall() { active = dcp::CallTiming{}; }
+    TimedCall(const TimedCall&) = delete;
+    TimedCall& operator=(const TimedCall&) = delete;
+
+    // Timing events travel with kernel dispatches, which a stream capture
+    // does not record: a timed call on a capturing stream is refused.
+    static int check(void* stream) {
+        if (active.start == nullptr && active.stop == nullptr) return DCP_OK;
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing((hipStream_t)stream, &st) != hipSuccess) return DCP_ERR_LAUNCH;
+        return st == hipStreamCaptureStatusNone ? DCP_OK : DCP_ERR_CAPTURE;
+    }
+};
+
 }  // namespace
+
+dcp::CallTiming& dcp::call_timing() { return active; }
 
 extern "C" {
 
@@ -61,6 +89,7 @@ const char* dcp_status_str(int status) {
         case DCP_ERR_ALIGN: return "DCP_ERR_ALIGN: payload not element-aligned or LSE not 4-byte aligned";
         case DCP_ERR_HEAD_RANGE: return "DCP_ERR_HEAD_RANGE: need 0 <= h0 < h1 <= H";
         case DCP_ERR_LAUNCH: return "DCP_ERR_LAUNCH: HIP kernel launch failed";
+        case DCP_ERR_CAPTURE: return "DCP_ERR_CAPTURE: timing events requested for a call on a capturing stream";
         default: return "unknown dcpmerge status";
     }
 }
@@ -72,6 +101,7 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
              const int32_t* kv_len, int64_t kl_R, int64_t kl_B,
              int64_t R, int64_t N, int64_t B, int64_t H, int64_t D,
              int dtype, void* stream) {
+    TimedCall timed;
     const int e = esize_of(dtype);
     if (e == 0) return DCP_ERR_DTYPE;
     if (R < 0 || B < 0 || N < 1 || H < 1 || D < 1) return DCP_ERR_SHAPE;
@@ -84,6 +114,7 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
     if (!aligned(src_o, e) || !aligned(dst_o, e) || !aligned(src_lse, 4) || !aligned(dst_lse, 4) ||
         (kv_len && !aligned(kv_len, 4)))
         return DCP_ERR_ALIGN;
+    if (int st = TimedCall::check(stream)) return st;
     dcp::PackArgs a;
     a.src = (const char*)src_o;
     a.src_lse = (const char*)src_lse;
@@ -107,6 +138,7 @@ int dcp_unpack_combine(const void* recv_o, int64_t ro_R, int64_t ro_N, int64_t r
                        float* out_lse, int64_t ol_R, int64_t ol_B, int64_t ol_H,
                        int64_t R, int64_t N, int64_t B, int64_t Hpr, int64_t D,
                        int dtype, int lse_base, void* stream) {
+    TimedCall timed;
     const int e = esize_of(dtype);
     if (e == 0) return DCP_ERR_DTYPE;
     if (lse_base != DCP_LSE_BASE_E && lse_base != DCP_LSE_BASE_2) return DCP_ERR_LSE_BASE;
@@ -118,6 +150,7 @@ int dcp_unpack_combine(const void* recv_o, int64_t ro_R, int64_t ro_N, int64_t r
     if (!recv_o || !recv_lse || !out) return DCP_ERR_NULL;
     if (!aligned(recv_o, e) || !aligned(out, e) || !aligned(recv_lse, 4) || (out_lse && !aligned(out_lse, 4)))
         return DCP_ERR_ALIGN;
+    if (int st = TimedCall::check(stream)) return st;
     if (N == 1) {
         // the world_size == 1 shortcut: out and out_lse are the partial and its LSE, unchanged
         dcp::PackArgs a;
@@ -157,6 +190,7 @@ int dcp_lse_combine_inplace(void* partial, int64_t p_N, int64_t p_T, int64_t p_H
                             int64_t N, int64_t P, int64_t rank0,
                             int64_t T, int64_t H, int64_t D,
                             int dtype, int lse_base, void* stream) {
+    TimedCall timed;
     const int e = esize_of(dtype);
     if (e == 0) return DCP_ERR_DTYPE;
     if (lse_base != DCP_LSE_BASE_E && lse_base != DCP_LSE_BASE_2) return DCP_ERR_LSE_BASE;
@@ -168,6 +202,7 @@ int dcp_lse_combine_inplace(void* partial, int64_t p_N, int64_t p_T, int64_t p_H
     if (!partial || !lse) return DCP_ERR_NULL;
     if (!aligned(partial, e) || (out && !aligned(out, e)) || !aligned(lse, 4) || (out_lse && !aligned(out_lse, 4)))
         return DCP_ERR_ALIGN;
+    if (int st = TimedCall::check(stream)) return st;
     if (N == 1) {
         // the world_size == 1 shortcut: the partial stays as it is; the slice is copied
         if (!out && !out_lse) return DCP_OK;
@@ -198,6 +233,12 @@ int dcp_lse_combine_inplace(void* partial, int64_t p_N, int64_t p_T, int64_t p_H
     a.dtype = dtype;
     a.base2 = lse_base == DCP_LSE_BASE_2;
     return launch_status(dcp::launch_inplace(a, (hipStream_t)stream));
+}
+
+int dcp_time_next_call(void* start_event, void* stop_event) {
+    armed.start = (hipEvent_t)start_event;
+    armed.stop = (hipEvent_t)stop_event;
+    return DCP_OK;
 }
 
 }  // extern "C"

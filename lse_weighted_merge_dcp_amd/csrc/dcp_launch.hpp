@@ -1,6 +1,7 @@
 // dcp_launch.hpp -- internal interface between the C ABI (api.cpp) and the
 // kernel launchers.  All strides here are in BYTES; the ABI converts.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,13 +63,31 @@ struct InplaceArgs {
     bool base2;
 };
 
+// Timing events the running entry-point call attaches to its own kernel
+// dispatches (requested with dcp_time_next_call).  `start` goes on the
+// call's first launch only; `stop` on every launch, so that it ends up on
+// the last one.  Both null: plain launches.
+struct CallTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+CallTiming& call_timing();  // the calling thread's, for the running call
+
 // Launch kernel(arg) and return that launch's own status.  (Reading the
 // thread's last error after a launch would also report, and clear, a stale
-// error the caller left from an unrelated call.)
+// error the caller left from an unrelated call.)  With timing events set the
+// events travel with the dispatch itself, so no marker is added to the
+// stream between kernels.
 template <typename Arg>
 inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream, const Arg& arg) {
     void* args[] = {const_cast<Arg*>(&arg)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+    CallTiming& t = call_timing();
+    if (t.start == nullptr && t.stop == nullptr)
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream, t.start,
+                                      t.stop, 0);
+    t.start = nullptr;
+    return e;
 }
 
 // Each launcher returns hipSuccess or the launch error; arguments are

@@ -13,6 +13,8 @@ torch.empty) and streams.  There is no CPU or PyTorch fallback.
       sglang PR #34213 report, code excerpt of cp_lse_ag_out_rs_mha
   lse_pack_dim(dtype), interleaved_views(send, D)
       vLLM PR #41160 report, 实现拆解 item 2; sglang PR #34651 report, 实现拆解 item 2
+  time_next_call(start, stop)
+      a measurement hook, not a step of the method: device time of one call
 
 Every entry point also accepts a leading R dimension (R independent calls
 in one launch, e.g. all simulated ranks stacked in one GPU's memory).
@@ -212,3 +214,14 @@ def cp_lse_combine_inplace(partial: torch.Tensor, lse: torch.Tensor, h0: int = 0
         _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(partial))
     _lib.check(st, "dcp_lse_combine_inplace")
     return (out, out_lse) if return_lse else out
+
+
+def time_next_call(start=None, stop=None) -> None:
+    """Attach timing events to the kernels of the next libdcpmerge call made
+    on this thread: `start` (a timing.Event or None) records when its first
+    kernel starts, `stop` when its last kernel ends.  The request covers one
+    call of the C library; a wrapper above that raises before reaching the
+    library leaves it pending.  A timed call on a capturing stream raises
+    DcpError (DCP_ERR_CAPTURE)."""
+    h = [None if e is None else e.handle for e in (start, stop)]
+    _lib.check(_lib.lib().dcp_time_next_call(h[0], h[1]), "dcp_time_next_call")

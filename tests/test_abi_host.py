@@ -32,7 +32,15 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["dcp_lse_combine_inplace", "dcp_lse_pack_dim", "dcp_pack",
-                                    "dcp_status_str", "dcp_unpack_combine"]
+                                    "dcp_status_str", "dcp_time_next_call", "dcp_unpack_combine"]
+
+
+def test_time_next_call_only_records_a_request():
+    """Arming and cancelling a timing request touches no device."""
+    lib = _lib.lib()
+    assert lib.dcp_time_next_call(None, None) == 0
+    assert lib.dcp_time_next_call(A, A + 256) == 0
+    assert lib.dcp_time_next_call(None, None) == 0
 
 
 def test_library_exports_every_declared_symbol():

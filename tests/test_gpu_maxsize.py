@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from lse_weighted_merge_dcp_amd import ops
+from lse_weighted_merge_dcp_amd import ops, timing
 from oracle import oracle as orc
 
 from helpers import check_lse, check_out, check_scaled, decode, say, to_host
@@ -49,6 +49,18 @@ def test_pack_beyond_one_launch():
     wp, ww = orc.interleaved_views_np(want, D, "bf16")
     orc.pack(to_host(src[bs], "bf16"), lse[bs].cpu().numpy(), wp, ww, N)
     assert np.array_equal(got, want)
+    # a timing request spans the whole call: first launch's start to last launch's end
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s, e = timing.Event(), timing.Event()
+    a.record()
+    ops.dcp_pack_a2a_send(src, lse, pay, words)
+    b.record()
+    ops.time_next_call(s, e)
+    ops.dcp_pack_a2a_send(src, lse, pay, words)
+    torch.cuda.synchronize()
+    whole, timed = a.elapsed_time(b) * 1e3, s.elapsed_us(e)
+    say("whole call %.0f us, timed %.0f us" % (whole, timed))
+    assert 0.7 * whole < timed < 1.3 * whole
     del src, lse, send, pay, words
     torch.cuda.empty_cache()
 
