@@ -76,7 +76,10 @@ def algorithmic_bytes(key, B=None):
       pack     2 N B H (D e + 4)     every rank reads and writes its rows
       combine  (N + 1) B H (D e + 4) N partial rows read, out + G written
       inplace  T H (N (4D + 4) + N 4D + 4D + 4)
-      kimi-rs combine  T H (N (4D + 4) + 4D + 4)."""
+      kimi-rs combine  T H (N (4D + 4) + 4D + 4)
+    and, for the Kimi-K3 workloads, one rank's own call in a real group:
+      inplace_rank  T H (2 4D + 4N)         scale its partial (P = 1)
+      combine_rank  T H/N (N (4D + 4) + 4D + 4)   its head slice."""
     from lse_weighted_merge_dcp_amd import synth
 
     w = synth.WORKLOADS["kimi" if key == "kimi-rs" else key]
@@ -84,10 +87,12 @@ def algorithmic_bytes(key, B=None):
         w = w.with_batch(B)
     if key == "kimi":
         row = 4 * w.D
-        return {"inplace": w.B * w.H * (w.N * (row + 4) + w.N * row + row + 4)}
+        return {"inplace": w.B * w.H * (w.N * (row + 4) + w.N * row + row + 4),
+                "inplace_rank": w.B * w.H * (2 * row + 4 * w.N)}
     if key == "kimi-rs":
         row = 4 * w.D
-        return {"combine": w.B * w.H * (w.N * (row + 4) + row + 4)}
+        return {"combine": w.B * w.H * (w.N * (row + 4) + row + 4),
+                "combine_rank": w.B * (w.H // w.N) * (w.N * (row + 4) + row + 4)}
     row = w.D * w.esize + 4
     per_th = w.B * w.H
     return {"pack": 2 * w.N * per_th * row, "combine": (w.N + 1) * per_th * row}
@@ -270,6 +275,20 @@ class InplaceWorkload:
     def kernels(self):
         return [("inplace", self.bytes_call, [self.run])]
 
+    def per_rank(self):
+        """What one GPU of a real DCP group runs: its own call (P = 1) that
+        scales its partial [T, H, D] in place by its weight from all N LSEs;
+        the sum over ranks is then the collective's.  Bytes: the partial read
+        and written back, and the N LSEs of every (token, head)."""
+        from lse_weighted_merge_dcp_amd import ops
+
+        nbytes = algorithmic_bytes("kimi", self.w.B)["inplace_rank"]
+
+        def call():
+            ops.cp_lse_combine_inplace(self.part[0:1], self.lse, rank0=0, want_out=False)
+
+        return [("inplace", nbytes, [call])]
+
     def named_step(self):
         return [("inplace", self.run)]
 
@@ -337,6 +356,28 @@ class ReduceScatterWorkload:
 
     def kernels(self):
         return [("combine", self.bytes_call, [self.run])]
+
+    def per_rank(self):
+        """What one GPU of a real DCP group runs: rank 0's combine of its
+        H/N-head slice of all N partials, as the exchange delivers it
+        (received slices contiguous, [N, T, H/N, D]; the copy that stands in
+        for the exchange is made once, untimed)."""
+        import torch
+
+        from lse_weighted_merge_dcp_amd import ops
+
+        hs = self.w.H // self.w.N
+        nbytes = algorithmic_bytes("kimi-rs", self.w.B)["combine_rank"]
+        recv = self.part[:, :, :hs].contiguous()
+        recv_lse = self.lse[:, :, :hs].contiguous()
+        out = torch.empty((self.w.B, hs, self.w.D), dtype=torch.float32, device=self.dev)
+        g = torch.empty((self.w.B, hs), dtype=torch.float32, device=self.dev)
+        torch.cuda.synchronize()
+
+        def call():
+            ops.dcp_lse_combine(recv, recv_lse, is_lse_base_on_e=True, out=out, out_lse=g)
+
+        return [("combine", nbytes, [call])]
 
     def named_step(self):
         return [("combine", self.run)]
@@ -626,12 +667,14 @@ def main():
     if hasattr(wl, "per_rank"):
         pr = {}
         for name, nbytes, launches in wl.per_rank():
-            us, _ = per_launch_us(launches, reps=max(3, args.steps // 4))
+            us, _ = per_launch_us(launches, reps=reps, restore=restore)
             pr[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
                         "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
-        pr["us_per_layer"] = round(sum(v["us_per_launch"] for v in pr.values()), 3)
+        if hasattr(wl, "hot_launches"):
+            pr["us_per_layer"] = round(sum(v["us_per_launch"] for v in pr.values()), 3)
         extra["per_rank"] = pr
-        us, _ = per_launch_us(wl.hot_launches(), reps=max(3, args.steps // 4))
+    if hasattr(wl, "hot_launches"):
+        us, _ = per_launch_us(wl.hot_launches(), reps=reps)
         extra["hot"] = {"us_per_layer": round(2 * us, 3),
                         "GBps": round(wl.bytes_layer / (2 * us * 1e-6) / 1e9, 1),
                         "note": "one layer's buffers reused by all layers (cache-resident)"}

@@ -17,7 +17,12 @@
 // line is touched once and is dead afterwards).  The fast path (P == N in
 // {2,4,8,16}, rank0 == 0: every rank stacked on this GPU) broadcasts weights
 // with row_newbcast; otherwise each lane recomputes the weight of the rank
-// it streams and applies the guards directly.  Guards in the fast path as in
+// it streams and applies the guards directly.  In that general path the
+// first block of held rows and their own LSEs load before the reduction,
+// which does not need them, so a wave's loads share one round trip; with a
+// single held partial (a rank scaling its own, the call each GPU of a real
+// group makes) a task is two consecutive segments of the row, so a wave
+// keeps twice the bytes in flight for one reduction.  Guards in the fast path as in
 // combine.hip: a finite row sum proves every scaled term finite; otherwise
 // the terms are re-formed from guarded values.  Blocks run in plain order
 // (measured faster than an XCD-contiguous order for these aligned rows).
@@ -49,8 +54,9 @@ __device__ __forceinline__ int lse_flags_i(float l) {
     return (__builtin_isnan(l) ? 1 : 0) | (l == INFINITY ? 2 : 0);
 }
 
-template <typename DT, int V, int LPR, int NT>
+template <typename DT, int V, int LPR, int NT, int PB, int U>
 __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
+    static_assert(NT == 0 || U == 1, "the stacked-ranks path takes one segment per row group");
     using C = Cvt<DT, V>;
     constexpr int EPV = C::n;
     constexpr uint32_t RPW = 64 / LPR;
@@ -64,14 +70,42 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
     if (task >= k.rows) return;  // whole row groups leave together
     const bool base2 = k.base2 != 0;
 
+    // a task is U consecutive segments of one row (k.steps tasks per row)
     const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
-    const uint32_t seg = task - row * k.steps;
+    const uint32_t seg = (task - row * k.steps) * U;
     const uint32_t t = fdiv(row, k.f_H);
     const uint32_t h = row - t * k.H;
     char* pbase = k.part + t * k.p_T + h * k.p_H;
     const char* lbase = k.lse + t * k.l_T + h * k.l_H;
     const bool in_slice = h >= k.h0 && h < k.h1;
     char* obase = (k.out != nullptr && in_slice) ? k.out + t * k.o_T + (h - k.h0) * k.o_H : nullptr;
+
+    // Lanes past the row's last chunk load that chunk again (in bounds) and
+    // store nothing.
+    bool on[U];
+    int64_t coff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t c = (seg + u) * LPR + li;
+        on[u] = c < k.chunks;
+        coff[u] = (int64_t)(on[u] ? c : k.chunks - 1u) * V;
+    }
+
+    // General path, in blocks of PB held partials: the first block's rows
+    // and LSEs do not depend on the reduction below, so they load before it
+    // and the wave's loads share one memory round trip.
+    Vec<V> x[NT > 0 ? 1 : U][NT > 0 ? 1 : PB];
+    float lw[NT > 0 ? 1 : PB];
+    if constexpr (NT == 0) {
+#pragma unroll
+        for (int q = 0; q < PB; ++q) {
+            if (q < (int)k.P) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[u][q] = vload_stream<V>(pbase + q * k.p_N + coff[u]);
+                lw[q] = load_f32(lbase + (int64_t)(k.rank0 + q) * k.l_N);
+            }
+        }
+    }
 
     // ---- global LSE over all N ranks -------------------------------------
     const int N = NT > 0 ? NT : (int)k.N;
@@ -119,12 +153,11 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
         [&]<int... I>(std::integer_sequence<int, I...>) { ((wi[I] = row_bcast<I>(w)), ...); }
         (std::make_integer_sequence<int, NT>{});
         {
-            const uint32_t c = seg * LPR + li;
-            if (c < k.chunks) {
-                const int64_t coff = (int64_t)c * V;
+            if (on[0]) {
+                const int64_t coff0 = coff[0];
                 Vec<V> x[NT];
 #pragma unroll
-                for (int i = 0; i < NT; ++i) x[i] = vload_stream<V>(pbase + i * k.p_N + coff);
+                for (int i = 0; i < NT; ++i) x[i] = vload_stream<V>(pbase + i * k.p_N + coff0);
                 float sc[NT][EPV];
                 float acc[EPV];
 #pragma unroll
@@ -155,61 +188,66 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < NT; ++i) vstore_stream<V>(pbase + i * k.p_N + coff, C::pack(sc[i]));
-                if (obase != nullptr) vstore<V>(obase + coff, C::pack(acc));
+                for (int i = 0; i < NT; ++i) vstore_stream<V>(pbase + i * k.p_N + coff0, C::pack(sc[i]));
+                if (obase != nullptr) vstore<V>(obase + coff0, C::pack(acc));
             }
         }
     } else {
         // ---- general path: any N, P held partials starting at rank0 -------
         // (not the stacked-ranks hot path: the guards are applied directly)
         const int P = (int)k.P;
-        constexpr int PB = 8;
-        {
-            const uint32_t c = seg * LPR + li;
-            if (c < k.chunks) {
-                const int64_t coff = (int64_t)c * V;
-                float acc[EPV];
+        float acc[U][EPV];
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) acc[e] = 0.0f;
-                for (int j0 = 0; j0 < P; j0 += PB) {
-                    Vec<V> x[PB];
-                    float wv[PB];
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-                    for (int q = 0; q < PB; ++q) {
-                        wv[q] = 0.0f;
-                        if (j0 + q < P) {
-                            x[q] = vload_stream<V>(pbase + (j0 + q) * k.p_N + coff);
-                            if (live)
-                                wv[q] = exp_base(load_f32(lbase + (int64_t)(k.rank0 + j0 + q) * k.l_N) - m, base2) / s;
-                        }
-                    }
+            for (int e = 0; e < EPV; ++e) acc[u][e] = 0.0f;
+        for (int j0 = 0; j0 < P; j0 += PB) {
+            if (j0 > 0) {
 #pragma unroll
-                    for (int q = 0; q < PB; ++q) {
-                        if (j0 + q < P) {
-                            float f[EPV];
-                            C::unpack(x[q], f);
+                for (int q = 0; q < PB; ++q) {
+                    if (j0 + q < P) {
 #pragma unroll
-                            for (int e = 0; e < EPV; ++e) {
-                                f[e] = guard_f(f[e]) * wv[q];
-                                acc[e] += f[e];
-                            }
-                            vstore_stream<V>(pbase + (j0 + q) * k.p_N + coff, C::pack(f));
-                        }
+                        for (int u = 0; u < U; ++u)
+                            x[u][q] = vload_stream<V>(pbase + (j0 + q) * k.p_N + coff[u]);
+                        lw[q] = load_f32(lbase + (int64_t)(k.rank0 + j0 + q) * k.l_N);
                     }
                 }
-                if (obase != nullptr) vstore<V>(obase + coff, C::pack(acc));
             }
+            float wv[PB];
+#pragma unroll
+            for (int q = 0; q < PB; ++q) wv[q] = (live && j0 + q < P) ? exp_base(lw[q] - m, base2) / s : 0.0f;
+#pragma unroll
+            for (int q = 0; q < PB; ++q) {
+                if (j0 + q < P) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        float f[EPV];
+                        C::unpack(x[u][q], f);
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) {
+                            f[e] = guard_f(f[e]) * wv[q];
+                            acc[u][e] += f[e];
+                        }
+                        if (on[u]) vstore_stream<V>(pbase + (j0 + q) * k.p_N + coff[u], C::pack(f));
+                    }
+                }
+            }
+        }
+        if (obase != nullptr) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (on[u]) vstore<V>(obase + coff[u], C::pack(acc[u]));
         }
     }
     if (k.olse != nullptr && in_slice && li == 0 && seg == 0)
         *reinterpret_cast<float*>(k.olse + t * k.ol_T + (h - k.h0) * k.ol_H) = G;
 }
 
-template <typename DT, int V, int LPR, int NT>
+template <typename DT, int V, int LPR, int NT, int PB = 8, int U = 1>
 hipError_t run(const InplaceArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR);
     const int64_t chunks = a.D * DT::esize / V;
-    const int64_t steps = (chunks + LPR - 1) / LPR;
+    const int64_t steps = ((chunks + LPR - 1) / LPR + U - 1) / U;  // tasks per row
     const int64_t t_chunk = max_units_per_launch(RPB) / (a.H * steps);
     for (int64_t t0 = 0; t0 < a.T; t0 += t_chunk) {
         const int64_t nt = t0 + t_chunk <= a.T ? t_chunk : a.T - t0;
@@ -236,7 +274,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
         k.f_steps = make_fastdiv(k.steps);
         k.base2 = a.base2 ? 1 : 0;
         const int64_t blocks = (rows + RPB - 1) / RPB;
-        const hipError_t e = launch_kernel(inplace_kernel<DT, V, LPR, NT>, dim3((uint32_t)blocks), dim3(256), stream, k);
+        const hipError_t e = launch_kernel(inplace_kernel<DT, V, LPR, NT, PB, U>, dim3((uint32_t)blocks), dim3(256), stream, k);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -253,6 +291,9 @@ hipError_t run_n(const InplaceArgs& a, hipStream_t stream) {
             default: break;
         }
     }
+    // one held partial (a rank scaling its own): single-row blocks keep the
+    // register budget, and the occupancy, of the smallest case
+    if (a.P == 1) return run<DT, V, LPR, 0, 1, 2>(a, stream);
     return run<DT, V, LPR, 0>(a, stream);
 }
 
@@ -263,6 +304,7 @@ hipError_t run_dt(const InplaceArgs& a, int V, hipStream_t stream) {
         if (chunks >= 48) return run_n<DT, 16, 64>(a, stream);
         return run_n<DT, 16, 16>(a, stream);
     }
+    if (a.P == 1) return run<DT, DT::esize, 64, 0, 1, 2>(a, stream);
     return run<DT, DT::esize, 64, 0>(a, stream);
 }
 

@@ -37,6 +37,9 @@ def test_algorithmic_bytes_per_layer():
     assert bench.algorithmic_bytes("kimi")["inplace"] == 16384 * 96 * 34_852 == 54_817_456_128
     # reduce-scatter flavour: no write-back
     assert bench.algorithmic_bytes("kimi-rs")["combine"] == 16384 * 96 * (8 * 2052 + 2052) == 29_047_652_352
+    # one rank's own calls: scale its partial (read + write back, N LSEs), combine its 12-head slice
+    assert bench.algorithmic_bytes("kimi")["inplace_rank"] == 16384 * 96 * (2 * 2048 + 8 * 4) == 6_492_782_592
+    assert bench.algorithmic_bytes("kimi-rs")["combine_rank"] == 16384 * 12 * (8 * 2052 + 2052) == 3_630_956_544
 
 
 def test_percentiles():

@@ -69,6 +69,35 @@ def test_inplace_held_subsets_and_dtypes(dt, N, P, rank0):
     check_scaled(decode(to_host(p, dt), dt), scaled, dt)
 
 
+@pytest.mark.parametrize("dt,D", [("f32", 512), ("f32", 520), ("f32", 192), ("bf16", 100), ("f16", 512),
+                                  ("bf16", 1000)])
+@pytest.mark.parametrize("want_out", [True, False])
+def test_inplace_single_rank_segment_groups(dt, D, want_out):
+    """P = 1, one rank scaling its own partial: each row group takes two
+    segments of a row.  Rows of an odd number of segments, a partly filled
+    second segment, rows that are not 16-byte multiples (element-wise path),
+    with and without the output slice."""
+    say("inplace single rank", dt, D, want_out)
+    N, T, H, rank0 = 8, 5, 12, 3
+    g = torch.Generator().manual_seed(D)
+    part = synth.to_storage(torch.randn(1, T, H, D, generator=g), dt)
+    part[0, 2, 7, D - 1] = synth.to_storage(torch.tensor([float("inf")]), dt)[0]
+    lse = np.random.default_rng(D).normal(0, 3, size=(N, T, H)).astype(np.float32)
+    lse[rank0, 1, 3] = np.nan
+    lse[:, 4, 0] = -np.inf
+    lse[5, 0, 9] = np.inf
+    p = to_dev(part, dt, DEV)
+    h0, h1 = 2, 11
+    res = ops.cp_lse_combine_inplace(p, torch.from_numpy(lse).to(DEV), h0=h0, h1=h1, rank0=rank0,
+                                     return_lse=want_out, want_out=want_out)
+    scaled, ref, gr, mag = orc.inplace(part, lse, dt, False, rank0=rank0, h0=h0, h1=h1)
+    check_scaled(decode(to_host(p, dt), dt), scaled, dt)
+    if want_out:
+        out, gg = res
+        check_out(decode(to_host(out, dt), dt), ref, mag, dt)
+        check_lse(gg.cpu().numpy(), gr)
+
+
 def test_inplace_scale_only_and_single_rank():
     rng = np.random.default_rng(3)
     part = rng.normal(size=(4, 3, 6, 64)).astype(np.float32)
