@@ -134,8 +134,16 @@ constexpr int kStreamU = 1;
 // ones 4-wave workgroups (measured: 1.5-2% faster on large launches, 1-3%
 // slower on small ones).
 constexpr int64_t kStreamWide = 32768;
+// Calls whose source partials span at least this many bytes read them with
+// the nontemporal hint (each source line is read once).  Above it a layer's
+// source and send buffers together outgrow the 256 MB Infinity Cache, and
+// keeping the dead source lines out of it leaves the send buffer there for
+// whoever reads it next (measured: the long-context B = 64 layer 5.8 ->
+// 6.0 TB/s, the combine after the pack 26.5 -> 21.9 us).  Below it the hint
+// costs 3% (the DeepSeek-V3-shaped pack, 67 MB of source).
+constexpr int64_t kStreamNtSourceBytes = int64_t(96) << 20;
 
-template <int U, int WPB>
+template <int U, int WPB, bool NTL>
 __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
@@ -171,7 +179,8 @@ __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) 
                 const bool has_lse = t < 4u;
                 const uint32_t base = j0 - row;               // source dword of the chunk's first payload dword
                 const char* sblk = k.src + r * k.s_R + b * k.s_B + (int64_t)(p * k.Hpr) * ((int64_t)(k.Wd - 1u) * 4);
-                Vec<16> x = neutral ? vzero<16>() : vload<16>(sblk + (int64_t)(has_lse ? base - 1u : base) * 4);
+                const char* sp = sblk + (int64_t)(has_lse ? base - 1u : base) * 4;
+                Vec<16> x = neutral ? vzero<16>() : (NTL ? vload_stream<16>(sp) : vload<16>(sp));
                 if (has_lse) {
                     uint32_t o[4];
 #pragma unroll
@@ -215,6 +224,7 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
     const int64_t lim = max_units_per_launch(4 * kStreamU);
     int64_t r_chunk = lim / per_r;
     int64_t b_chunk = a.B;
+    const bool nt_source = a.R * a.B * a.H * a.row_bytes >= kStreamNtSourceBytes;
     if (r_chunk < 1) {
         r_chunk = 1;
         b_chunk = lim / (N * S);
@@ -246,10 +256,13 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             hipError_t e;
             if (k.nsteps >= kStreamWide) {
                 const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
-                e = launch_kernel(pack_stream_kernel<kStreamU, 8>, dim3(blocks), dim3(512), stream, k);
+                if (nt_source)
+                    e = launch_kernel(pack_stream_kernel<kStreamU, 8, true>, dim3(blocks), dim3(512), stream, k);
+                else
+                    e = launch_kernel(pack_stream_kernel<kStreamU, 8, false>, dim3(blocks), dim3(512), stream, k);
             } else {
                 const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-                e = launch_kernel(pack_stream_kernel<kStreamU, 4>, dim3(blocks), dim3(256), stream, k);
+                e = launch_kernel(pack_stream_kernel<kStreamU, 4, false>, dim3(blocks), dim3(256), stream, k);
             }
             if (e != hipSuccess) return e;
         }
