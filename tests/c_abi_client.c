@@ -14,7 +14,9 @@
  * the payload type; DIR/lse.bin the LSEs [N, B, H] fp32.  Written: DIR/send.bin
  * (the send buffers [N src, N peer, B, H/N, D + lpd]), DIR/comb.bin (the
  * merged rows [N dst, B, H/N, D]) and DIR/g.bin (the global LSE [N, B, H/N]).
- * The caller checks them against the oracle.  Exit status 0 on success.
+ * The caller checks them against the oracle.  The combine is timed with
+ * dcp_time_next_call (printed as "timed combine: ... us").  Exit status 0 on
+ * success.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -110,7 +112,13 @@ int main(int argc, char** argv) {
                   N, N, B, H, D, dtype, stream);
     if (st != DCP_OK) { fprintf(stderr, "dcp_pack: %s\n", dcp_status_str(st)); return 1; }
 
-    /* combine: destination p reads send[:, p] -- axes (dst, src) swapped */
+    /* combine: destination p reads send[:, p] -- axes (dst, src) swapped;
+     * its kernels carry timing events on their own dispatches */
+    hipEvent_t ev0, ev1;
+    HIP_OK(hipEventCreateWithFlags(&ev0, hipEventDisableSystemFence));
+    HIP_OK(hipEventCreateWithFlags(&ev1, hipEventDisableSystemFence));
+    st = dcp_time_next_call(ev0, ev1);
+    if (st != DCP_OK) { fprintf(stderr, "dcp_time_next_call: %s\n", dcp_status_str(st)); return 1; }
     st = dcp_unpack_combine(d_send, sN, sR, sB, sH,
                             d_words, sN * e / 4, sR * e / 4, sB * e / 4, sH * e / 4,
                             d_comb, B * Hpr * D, Hpr * D, D,
@@ -118,6 +126,12 @@ int main(int argc, char** argv) {
                             N, N, B, Hpr, D, dtype, base, stream);
     if (st != DCP_OK) { fprintf(stderr, "dcp_unpack_combine: %s\n", dcp_status_str(st)); return 1; }
     HIP_OK(hipStreamSynchronize(stream));
+    float ms = 0.0f;
+    HIP_OK(hipEventElapsedTime(&ms, ev0, ev1));
+    if (!(ms > 0.0f)) { fprintf(stderr, "timed combine: %g ms\n", ms); return 1; }
+    printf("timed combine: %.3f us\n", ms * 1e3);
+    HIP_OK(hipEventDestroy(ev0));
+    HIP_OK(hipEventDestroy(ev1));
 
     void* h_send = malloc(send_bytes);
     void* h_comb = malloc(comb_bytes);

@@ -42,6 +42,7 @@ def test_c_client_pack_and_combine(tmp_path, dt, N, B, H, D, base2):
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stderr
     assert "rejected call: DCP_ERR_NULL" in r.stdout
+    assert "timed combine: " in r.stdout
 
     lpd = 4 // np.dtype(NP_DT[dt]).itemsize
     Hpr = H // N
