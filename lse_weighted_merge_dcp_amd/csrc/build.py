@@ -24,7 +24,7 @@ ARCH = "gfx950"
 # pass warns that it does not know the feature, which is harmless.
 HIP_FLAGS = ["-O3", "-std=c++20", "-fPIC", "--offload-arch=" + ARCH,
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
+             "-Wall", "-Wextra", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
 
 def hipcc() -> str:

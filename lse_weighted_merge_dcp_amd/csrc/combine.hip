@@ -51,9 +51,11 @@ struct CombK {
     int base2;
 };
 
-// Global LSE of a row from the l_j held by the 16 lanes of each DPP row
-// (lanes past N hold -inf).  Returns G; sets e = beta^(l_j - m) and s = sum e
-// when G is finite (live), else live = false and every weight is 0.
+// Special values and maximum of a row's LSEs, from the l_j (NaN replaced by
+// -inf) and flags held by the 16 lanes of each DPP row (lanes past N hold
+// -inf).  NaN, +inf or all -inf decide G here and leave live = false (every
+// weight 0); otherwise live = true and the caller completes G = m +
+// log_beta(s) once it has summed s = sum beta^(l_j - m).
 struct LseState {
     float G;
     float m;
@@ -61,7 +63,7 @@ struct LseState {
     bool live;
 };
 
-__device__ __forceinline__ LseState reduce_lse(float l_max_in, int flags_in, bool base2) {
+__device__ __forceinline__ LseState reduce_lse(float l_max_in, int flags_in) {
     LseState st;
     const int flags = row_or(flags_in);
     const float m = row_max(l_max_in);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
         Vec<V> x[NT];
 #pragma unroll
         for (int i = 0; i < NT; ++i) x[i] = vload_stream<V>(rbase + i * k.r_N + coff);
-        LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj), base2);
+        LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj));
         float w = 0.0f;
         if (st.live) {
             const float e = (j < (uint32_t)NT) ? exp_base(lj - st.m, base2) : 0.0f;
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
             fl |= lse_flags(l);
             if (!__builtin_isnan(l)) lmax = fmaxf(lmax, l);
         }
-        LseState st = reduce_lse(lmax, fl, base2);
+        LseState st = reduce_lse(lmax, fl);
         float s = 1.0f;
         if (st.live) {
             float part = 0.0f;
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
 #pragma unroll
         for (int i = 0; i < NT; ++i) x[i] = gload16<true>(wave_addr(rbase + i * k.r_N), voff);
     }
-    LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj), base2);
+    LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj));
     float w = 0.0f;
     if (st.live) {
         const float e = (j < (uint32_t)NT) ? exp_base(lj - st.m, base2) : 0.0f;
