@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 // weights measured faster, and the launcher picks by size.  Small launches
 // also use one-wave workgroups (WPB = 1): the rows then spread over up to
 // four times as many CUs, and each CU's load pipeline serves fewer of them.
-template <typename DT, int NT, bool HOIST, int WPB>
+template <typename DT, int NT, bool HOIST, int WPB, bool NTS>
 __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     using C = Cvt<DT, 16>;
     constexpr int EPV = C::n;
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
             for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
         }
     }
-    if (on) vstore<16>(obase + voff, C::pack(acc));
+    if (on) vstore_out<16, NTS>(obase + voff, C::pack(acc));
     if (k.olse != nullptr && lane == 0 && seg == 0)
         *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
 }
@@ -347,6 +347,7 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
     const int64_t per_r = a.B * a.Hpr * steps;
     const int64_t lim = max_units_per_launch(RPB);
     int64_t r_chunk = per_r > 0 ? lim / per_r : a.R;
+    const bool nt_out = a.R * a.B * a.Hpr * a.D * DT::esize >= kNtOutputBytes;
     int64_t b_chunk = a.B;
     if (r_chunk < 1) {
         r_chunk = 1;
@@ -380,9 +381,14 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             hipError_t e;
             if constexpr (V == 16 && LPR == 64 && NT > 0) {
                 if (rows <= kHoistMaxRows)
-                    e = launch_kernel(combine_wave_kernel<DT, NT, true, 1>, dim3((uint32_t)rows), dim3(64), stream, k);
+                    e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false>, dim3((uint32_t)rows), dim3(64), stream,
+                                      k);
+                else if (nt_out)
+                    e = launch_kernel(combine_wave_kernel<DT, NT, false, 4, true>, dim3((uint32_t)blocks), dim3(256),
+                                      stream, k);
                 else
-                    e = launch_kernel(combine_wave_kernel<DT, NT, false, 4>, dim3((uint32_t)blocks), dim3(256), stream, k);
+                    e = launch_kernel(combine_wave_kernel<DT, NT, false, 4, false>, dim3((uint32_t)blocks), dim3(256),
+                                      stream, k);
             } else {
                 e = launch_kernel(combine_kernel<DT, V, LPR, NT>, dim3((uint32_t)blocks), dim3(256), stream, k);
             }

@@ -104,6 +104,11 @@ template <int V> __device__ __forceinline__ Vec<V> vload_stream(const char* p) {
 template <int V> __device__ __forceinline__ void vstore_stream(char* p, const Vec<V>& v) {
     if constexpr (V == 16) vstore16_stream(p, v); else vstore<V>(p, v);
 }
+// Output stores, streaming or not.  A compile-time choice: the compiler merges
+// a runtime branch between the two stores into one plain store.
+template <int V, bool NTS> __device__ __forceinline__ void vstore_out(char* p, const Vec<V>& v) {
+    if constexpr (NTS) vstore_stream<V>(p, v); else vstore<V>(p, v);
+}
 
 __device__ __forceinline__ uint32_t load_word(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
 __device__ __forceinline__ void store_word(char* p, uint32_t w) { *reinterpret_cast<uint32_t*>(p) = w; }

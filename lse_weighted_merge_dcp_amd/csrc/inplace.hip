@@ -54,7 +54,7 @@ __device__ __forceinline__ int lse_flags_i(float l) {
     return (__builtin_isnan(l) ? 1 : 0) | (l == INFINITY ? 2 : 0);
 }
 
-template <typename DT, int V, int LPR, int NT, int PB, int U>
+template <typename DT, int V, int LPR, int NT, int PB, int U, bool NTS>
 __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
     static_assert(NT == 0 || U == 1, "the stacked-ranks path takes one segment per row group");
     using C = Cvt<DT, V>;
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
                 }
 #pragma unroll
                 for (int i = 0; i < NT; ++i) vstore_stream<V>(pbase + i * k.p_N + coff0, C::pack(sc[i]));
-                if (obase != nullptr) vstore<V>(obase + coff0, C::pack(acc));
+                if (obase != nullptr) vstore_out<V, NTS>(obase + coff0, C::pack(acc));
             }
         }
     } else {
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void inplace_kernel(const InplK k) {
         *reinterpret_cast<float*>(k.olse + t * k.ol_T + (h - k.h0) * k.ol_H) = G;
 }
 
-template <typename DT, int V, int LPR, int NT, int PB = 8, int U = 1>
+template <typename DT, int V, int LPR, int NT, int PB = 8, int U = 1, bool NTS = false>
 hipError_t run(const InplaceArgs& a, hipStream_t stream) {
     constexpr int64_t RPB = 4 * (64 / LPR);
     const int64_t chunks = a.D * DT::esize / V;
@@ -274,7 +274,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
         k.f_steps = make_fastdiv(k.steps);
         k.base2 = a.base2 ? 1 : 0;
         const int64_t blocks = (rows + RPB - 1) / RPB;
-        const hipError_t e = launch_kernel(inplace_kernel<DT, V, LPR, NT, PB, U>, dim3((uint32_t)blocks), dim3(256), stream, k);
+        const hipError_t e = launch_kernel(inplace_kernel<DT, V, LPR, NT, PB, U, NTS>, dim3((uint32_t)blocks), dim3(256), stream, k);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -283,6 +283,17 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
 template <typename DT, int V, int LPR>
 hipError_t run_n(const InplaceArgs& a, hipStream_t stream) {
     if (a.P == a.N && a.rank0 == 0) {
+        // a merged slice too large to stay cached for its reader goes out with
+        // the nontemporal hint
+        if (a.out != nullptr && a.T * (a.h1 - a.h0) * a.D * DT::esize >= kNtOutputBytes) {
+            switch (a.N) {
+                case 2: return run<DT, V, LPR, 2, 8, 1, true>(a, stream);
+                case 4: return run<DT, V, LPR, 4, 8, 1, true>(a, stream);
+                case 8: return run<DT, V, LPR, 8, 8, 1, true>(a, stream);
+                case 16: return run<DT, V, LPR, 16, 8, 1, true>(a, stream);
+                default: break;
+            }
+        }
         switch (a.N) {
             case 2: return run<DT, V, LPR, 2>(a, stream);
             case 4: return run<DT, V, LPR, 4>(a, stream);
