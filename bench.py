@@ -414,28 +414,51 @@ class ReduceScatterWorkload:
 # --------------------------------------------------------------------------
 # timing
 # --------------------------------------------------------------------------
-def copy_ceiling_gbs(dev, nbytes=2 << 30, reps=10):
-    """Achievable HBM rate of a plain device-to-device copy of nbytes (read
-    nbytes + write nbytes), timed with HIP events: the practical ceiling."""
+def _median_event_s(fn, reps):
     import torch
 
-    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-    b = torch.empty_like(a)
-    b.copy_(a)
+    fn()
     torch.cuda.synchronize()
     times = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        b.copy_(a)
+        fn()
         e1.record()
         e1.synchronize()
         times.append(e0.elapsed_time(e1) * 1e-3)
-    del a, b
-    torch.cuda.empty_cache()
     times.sort()
-    return 2 * nbytes / times[len(times) // 2] / 1e9
+    return times[len(times) // 2]
+
+
+def copy_ceiling_gbs(dev, nbytes=2 << 30, reps=10):
+    """HBM rate of two plain copies of nbytes (read nbytes + write nbytes),
+    timed with HIP events on the stream they run on: the runtime's
+    device-to-device copy (torch copy_), and the library's own row copy (the
+    N = 1 identity of dcp_unpack_combine: 1 KB rows copied bit for bit with
+    16-byte vectors, the LSE word beside each row).  Returns
+    {"runtime": GB/s, "library_row_copy": GB/s}."""
+    import torch
+
+    from lse_weighted_merge_dcp_amd import ops
+
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    runtime = 2 * nbytes / _median_event_s(lambda: b.copy_(a), reps) / 1e9
+    del b
+    # the same bytes as [1, T, 1, 256] fp32 rows of 1 KB with one LSE each
+    T = nbytes // 1024
+    src = a.view(1, T, 1, 256)
+    lse = torch.zeros((1, T, 1), dtype=torch.float32, device=dev)
+    out = torch.empty((T, 1, 256), dtype=torch.float32, device=dev)
+    g = torch.empty((T, 1), dtype=torch.float32, device=dev)
+    moved = 2 * (nbytes + 4 * T)
+    library = moved / _median_event_s(
+        lambda: ops.dcp_lse_combine(src, lse, is_lse_base_on_e=True, out=out, out_lse=g), reps) / 1e9
+    del a, src, lse, out, g
+    torch.cuda.empty_cache()
+    return {"runtime": runtime, "library_row_copy": library}
 
 
 def percentiles(xs):
@@ -678,7 +701,8 @@ def main():
         extra["hot"] = {"us_per_layer": round(2 * us, 3),
                         "GBps": round(wl.bytes_layer / (2 * us * 1e-6) / 1e9, 1),
                         "note": "one layer's buffers reused by all layers (cache-resident)"}
-    ceiling = copy_ceiling_gbs(dev)
+    ceilings = copy_ceiling_gbs(dev)
+    ceiling = max(ceilings.values())
     dom = max(kinfo, key=lambda k: kinfo[k]["us_per_launch"])
     achieved = kinfo[dom]["GBps"]
     traffic = load_traffic(args.workload, wl, dom)
@@ -717,6 +741,7 @@ def main():
         "us_per_layer": round(ms_per_step * 1e3 / layers, 3),
         "step_ms": percentiles(step_ms),
         "copy_ceiling_GBps": round(ceiling, 1),
+        "copy_ceilings_GBps": {k: round(v, 1) for k, v in ceilings.items()},
         "pct_of_copy_ceiling": round(100.0 * gbs / ceiling, 2),
         "bytes_per_step": wl.step_bytes(),
         "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
