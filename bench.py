@@ -531,6 +531,9 @@ def in_step_us(named, reps, restore=None):
     The step's calls are issued eagerly, in the step's order, behind a
     GPU-side wait (torch.cuda._sleep) that outlasts the host's enqueueing,
     so that the device runs them back to back as it runs the step graph.
+    (A torch without _sleep runs the replays without that wait; the host
+    may then fall behind the device, which leaves gaps between kernels but
+    not inside the timed ones.)
     The launches of one kernel per replay carry timing events on their own
     dispatches (ops.time_next_call), so no marker packet sits between the
     kernels; the replays take the kernels in turn.  `named` is the step as
