@@ -595,7 +595,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload)
+        summarize_counters(args.summarize_counters, args.workload, args.B)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -708,7 +708,7 @@ def main():
     ceiling = max(ceilings.values())
     dom = max(kinfo, key=lambda k: kinfo[k]["us_per_launch"])
     achieved = kinfo[dom]["GBps"]
-    traffic = load_traffic(args.workload, wl, dom)
+    traffic = load_traffic(counter_key(args.workload, args.B), wl, dom)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -786,8 +786,18 @@ def counter_run(wl):
         print("# counter run: %s x3, %d algorithmic bytes per launch" % (name, nbytes), flush=True)
 
 
-def load_traffic(workload, wl, kernel):
-    p = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+def counter_key(workload, B=None):
+    """Name of a workload's counter summary (profiles/counters_<key>.json):
+    the long-context sweep keeps one per batch size."""
+    if workload == "longctx":
+        from lse_weighted_merge_dcp_amd import synth
+
+        return "longctx_B%d" % (B if B is not None else synth.WORKLOADS["longctx"].B)
+    return workload
+
+
+def load_traffic(key, wl, kernel):
+    p = os.path.join(ROOT, "profiles", "counters_%s.json" % key)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -796,7 +806,7 @@ def load_traffic(workload, wl, kernel):
     return d["kernels"][kernel]["hbm_bytes_per_launch"]
 
 
-def summarize_counters(directory, workload):
+def summarize_counters(directory, workload, B=None):
     """rocprofv3 --pmc CSVs (FETCH_SIZE run and WRITE_SIZE run) -> per-launch
     HBM bytes of each kernel, scaled by the copy reference."""
     import csv
@@ -826,7 +836,8 @@ def summarize_counters(directory, workload):
         raise SystemExit("no copy-reference counters found in %s" % directory)
     fs = copy_bytes / f_copy       # bytes per counter unit, from a copy of known size
     ws = copy_bytes / w_copy
-    out = {"kernel_source": kernel_source_hash(), "workload": workload,
+    key = counter_key(workload, B)
+    out = {"kernel_source": kernel_source_hash(), "workload": workload, "key": key,
            "copy_reference": {"bytes": copy_bytes, "FETCH_SIZE": f_copy, "WRITE_SIZE": w_copy,
                               "fetch_scale": fs, "write_scale": ws}, "kernels": {}}
     for kname, pat in (("pack", r"\bpack_(stream_)?kernel"), ("combine", r"\bcombine_(wave_)?kernel"),
@@ -837,25 +848,29 @@ def summarize_counters(directory, workload):
             continue
         out["kernels"][kname] = {"FETCH_SIZE": f, "WRITE_SIZE": wv, "read_bytes": f * fs, "write_bytes": wv * ws,
                                  "hbm_bytes_per_launch": f * fs + wv * ws}
-    alg = algorithmic_bytes(workload)
+    if workload == "longctx":
+        out["B"] = int(key[len("longctx_B"):])
+    alg = algorithmic_bytes(workload, out.get("B"))
     for kname, v in out["kernels"].items():
         v["algorithmic_bytes_per_launch"] = alg.get(kname)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "counters_%s.json" % workload), "w") as fo:
+    with open(os.path.join(ROOT, "profiles", "counters_%s.json" % key), "w") as fo:
         json.dump(out, fo, indent=1)
-    with open(os.path.join(ROOT, "profiles", "counters_%s.md" % workload), "w") as fo:
+    with open(os.path.join(ROOT, "profiles", "counters_%s.md" % key), "w") as fo:
         fo.write(counters_markdown(out, directory))
     print(json.dumps(out, indent=1))
 
 
 def counters_markdown(d, directory):
     w = d["workload"]
+    key = d.get("key", w)
+    wargs = w + (" --B %d" % d["B"] if "B" in d else "")
     dirs = directory.split(",")
     c = d["copy_reference"]
     lines = [
-        "# HBM traffic counters: %s workload" % w,
+        "# HBM traffic counters: %s workload%s" % (w, " (B = %d)" % d["B"] if "B" in d else ""),
         "",
-        "Kernel source hash `%s` (`counters_%s.json`; bench.py reports these bytes as" % (d["kernel_source"], w),
+        "Kernel source hash `%s` (`counters_%s.json`; bench.py reports these bytes as" % (d["kernel_source"], key),
         "`roofline.traffic` only while the kernel sources still hash to it).  Two rocprofv3",
         "counter runs of the same short program (`bench.py --counter-run`: a 1 GiB",
         "`torch.neg` pass as the scale reference, then three launches of each kernel on",
@@ -864,10 +879,10 @@ def counters_markdown(d, directory):
         "```",
         "cd /tmp && export TMPDIR=/tmp",
         "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/%s -o run -- python3 $REPO/bench.py --workload %s --counter-run"
-        % (dirs[0], w),
+        % (dirs[0], wargs),
         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/%s -o run -- python3 $REPO/bench.py --workload %s --counter-run"
-        % (dirs[-1], w),
-        "python3 bench.py --workload %s --summarize-counters %s" % (w, directory),
+        % (dirs[-1], wargs),
+        "python3 bench.py --workload %s --summarize-counters %s" % (wargs, directory),
         "```",
         "",
         "Scale reference: `torch.neg` over 2^28 fp32 reads and writes exactly 1 GiB; it",
