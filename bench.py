@@ -1,6 +1,6 @@
 """Benchmark of the DCP partial-merge path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload dsv3|longctx|split|tiny|kimi|kimi-rs] [--B 64]
+    python bench.py [--steps K] [--warmup W] [--workload dsv3|longctx|split|tiny|kimi|kimi-rs|dsv3fp8] [--B 64]
 
 Default workload: DeepSeek-V3-shaped MLA decode -- N=8 simulated DCP ranks,
 B=64 tokens, H=128 heads (16 per rank), D=512 (kv_lora_rank), bf16 partials,
@@ -15,9 +15,10 @@ graph and replayed K times; inputs are in HBM before timing starts.
 Printed: one JSON line with the whole-step throughput in GB/s of algorithmic
 bytes (what the method must move: (3N+1)(D*e+4) bytes per (token, head) for
 pack + combine), microseconds per layer, the roofline entry of the dominant
-kernel (per-launch duration from HIP events on the launch stream, over a
-replayed graph of that kernel's launches) and the CPU oracle timed on a
-bounded sample, on every host thread and on one.  Beside them: the p10/p50/p90 step time, the rate of a plain
+kernel (its per-launch duration inside the step, from HIP events attached to
+its own dispatches in eager replays of the step; the same kernel's launches
+replayed back to back on cold buffers give `cold_achieved`) and the CPU
+oracle timed on a bounded sample, on every host thread and on one.  Beside them: the p10/p50/p90 step time, the rate of a plain
 2 GiB device-to-device copy measured in the same run (the practical ceiling),
 and for the pack + combine workloads the per-rank share (one rank's pack and
 one destination's combine at their real shapes) and the cache-resident step
@@ -26,7 +27,8 @@ one destination's combine at their real shapes) and the cache-resident step
 Other workloads: longctx (N=16, H=128, bf16, --B 1..512), split (peer-inside
 split layout, fp16), tiny (N=2 fp32), kimi (in-place merge over 8 ranks'
 [16384, 96, 512] fp32 partials), kimi-rs (the same merge, reduce-scatter
-flavour: each rank's head slice, no partial write-back).
+flavour: each rank's head slice, no partial write-back), dsv3fp8 (the
+DeepSeek-V3 shape with an OCP FP8 E4M3 payload: rows of D + 4 bytes).
 
 Other modes:
   --counter-run       run a 1 GiB plain copy and a few launches of each kernel
@@ -111,13 +113,16 @@ class A2AWorkload:
         if B is not None:
             w = w.with_batch(B)
         self.w, self.layers, self.dev = w, layers, dev
-        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8": torch.float8_e4m3fn}[w.dtype]
         t0 = time.time()
         self.inp = synth.rank_inputs(w)
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
         o = self.inp["out"]
         if w.dtype == "bf16":
             o0 = torch.from_numpy(o.view(np.int16)).to(dev).view(torch.bfloat16)
+        elif w.dtype == "fp8":
+            o0 = torch.from_numpy(o).to(dev).view(torch.float8_e4m3fn)
         else:
             o0 = torch.from_numpy(o).to(dev)
         l0 = torch.from_numpy(self.inp["lse"]).to(dev)
@@ -204,7 +209,8 @@ class A2AWorkload:
         return {"workload": "%s: N=%d simulated ranks, B=%d, H=%d (%d per rank), D=%d %s, base-%s LSE, %s layout, "
                             "%d layers per step" % (
                                 {"dsv3": "DeepSeek-V3-shaped MLA decode", "longctx": "long-context decode sweep",
-                                 "split": "peer-inside split layout", "tiny": "tiny merge"}[w.key],
+                                 "split": "peer-inside split layout", "tiny": "tiny merge",
+                                 "dsv3fp8": "DeepSeek-V3-shaped MLA decode, fp8 payload"}[w.key],
                                 w.N, w.B, w.H, w.Hpr, w.D, w.dtype, "2" if w.base2 else "e", w.layout,
                                 self.layers),
                 "N": w.N, "B": w.B, "H": w.H, "D": w.D, "layers": self.layers, "layout": w.layout,
@@ -219,7 +225,7 @@ class A2AWorkload:
 
         w, inp = self.w, self.inp
         lpd = 4 // w.esize
-        npdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+        npdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}[w.dtype]
         done, t_total = 0, 0.0
         while True:
             t0 = time.perf_counter()
@@ -586,7 +592,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3", choices=["dsv3", "longctx", "split", "tiny", "kimi", "kimi-rs"])
+    ap.add_argument("--workload", default="dsv3",
+                    choices=["dsv3", "longctx", "split", "tiny", "kimi", "kimi-rs", "dsv3fp8"])
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--layers", type=int, default=61)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")

@@ -50,8 +50,16 @@
 extern "C" {
 #endif
 
-/* Element type of the partial outputs.  LSEs are always fp32. */
-typedef enum { DCP_F32 = 0, DCP_F16 = 1, DCP_BF16 = 2 } dcp_dtype;
+/* Element type of the partial outputs.  LSEs are always fp32.
+ * DCP_FP8_E4M3 is the OCP FP8 E4M3 format (e4m3fn: bias 7, 3 mantissa bits,
+ * subnormals, S.1111.111 = NaN, no infinities, largest finite 448).  The
+ * pages mention fp8 only as a future dtype whose word alignment would need
+ * review (sglang PR #34651 report, 风险与影响) and which the vLLM helper
+ * rejects (vLLM PR #41160 report, 风险与影响); here it follows the same
+ * rules as the other types: lpd = 4 / element size = 4, so an interleaved
+ * row is D + 4 bytes and needs D % 4 == 0 to keep its LSE word aligned, and
+ * merged outputs are rounded to nearest even in fp8. */
+typedef enum { DCP_F32 = 0, DCP_F16 = 1, DCP_BF16 = 2, DCP_FP8_E4M3 = 3 } dcp_dtype;
 
 /* Base of the LSE values.  Attention kernels differ (trtllm-gen emits base 2,
  * cute-dsl natural log), so the base is a flag of the merge itself
@@ -75,9 +83,10 @@ enum {
 };
 
 /* Number of payload elements one fp32 LSE occupies when it is interleaved at
- * the tail of a payload row: 1 for DCP_F32, 2 for DCP_F16 and DCP_BF16
- * (vLLM PR #41160 report, 实现拆解 item 2; bf16 is 2 like fp16).  Returns
- * DCP_ERR_DTYPE for anything else (the page raises ValueError for fp8). */
+ * the tail of a payload row: 1 for DCP_F32, 2 for DCP_F16 and DCP_BF16, 4 for
+ * DCP_FP8_E4M3 (vLLM PR #41160 report, 实现拆解 item 2: 4 bytes over the
+ * element size; bf16 is 2 like fp16).  Returns DCP_ERR_DTYPE for anything
+ * else. */
 int dcp_lse_pack_dim(int dtype);
 
 /* Static, human-readable text of a status code. */

@@ -10,7 +10,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcpmerge.so")
 
-DCP_F32, DCP_F16, DCP_BF16 = 0, 1, 2
+DCP_F32, DCP_F16, DCP_BF16, DCP_FP8_E4M3 = 0, 1, 2, 3
 DCP_LSE_BASE_E, DCP_LSE_BASE_2 = 0, 1
 
 STATUS = {

@@ -17,6 +17,7 @@ int esize_of(int dtype) {
         case DCP_F32: return 4;
         case DCP_F16: return 2;
         case DCP_BF16: return 2;
+        case DCP_FP8_E4M3: return 1;
         default: return 0;
     }
 }

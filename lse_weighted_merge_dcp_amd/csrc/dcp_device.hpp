@@ -23,6 +23,7 @@ template <> struct Vec<16> { uint32_t w[4]; };
 template <> struct Vec<8>  { uint32_t w[2]; };
 template <> struct Vec<4>  { uint32_t w[1]; };
 template <> struct Vec<2>  { uint16_t h; };
+template <> struct Vec<1>  { uint8_t b; };
 
 template <int V> __device__ __forceinline__ Vec<V> vload(const char* p);
 template <> __device__ __forceinline__ Vec<16> vload<16>(const char* p) {
@@ -38,6 +39,9 @@ template <> __device__ __forceinline__ Vec<4> vload<4>(const char* p) {
 }
 template <> __device__ __forceinline__ Vec<2> vload<2>(const char* p) {
     Vec<2> v; v.h = *reinterpret_cast<const uint16_t*>(p); return v;
+}
+template <> __device__ __forceinline__ Vec<1> vload<1>(const char* p) {
+    Vec<1> v; v.b = *reinterpret_cast<const uint8_t*>(p); return v;
 }
 
 template <int V> __device__ __forceinline__ Vec<V> vzero() {
@@ -59,6 +63,9 @@ template <> __device__ __forceinline__ void vstore<4>(char* p, const Vec<4>& v) 
 }
 template <> __device__ __forceinline__ void vstore<2>(char* p, const Vec<2>& v) {
     *reinterpret_cast<uint16_t*>(p) = v.h;
+}
+template <> __device__ __forceinline__ void vstore<1>(char* p, const Vec<1>& v) {
+    *reinterpret_cast<uint8_t*>(p) = v.b;
 }
 
 // A wave-uniform address held in scalar registers: loads from it plus a
@@ -124,6 +131,7 @@ typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
 struct F32T  { static constexpr int esize = 4; };
 struct F16T  { static constexpr int esize = 2; };
 struct BF16T { static constexpr int esize = 2; };
+struct FP8T  { static constexpr int esize = 1; };   // OCP FP8 E4M3 (e4m3fn)
 
 template <typename DT, int V> struct Cvt;
 
@@ -203,6 +211,65 @@ template <> struct Cvt<BF16T, 2> {
     }
     static __device__ __forceinline__ Vec<2> pack(const float* f) {
         Vec<2> v; v.h = __builtin_bit_cast(uint16_t, (__bf16)f[0]); return v;
+    }
+};
+
+// 8-bit payload, OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa
+// bits; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN;
+// there are no infinities and the largest finite magnitude is 448.
+// Decoding uses gfx950's packed conversion (two bytes of a word per
+// instruction, exact).  Encoding rounds to nearest even in integer
+// arithmetic: a merged value is a convex combination of fp8 values, so it
+// never exceeds 448 in magnitude; anything at or beyond 448 (which the merge
+// does not produce) saturates to +-448, and NaN stays NaN.
+__device__ __forceinline__ uint32_t fp8_e4m3_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t c;
+    if (a > 0x7f800000u) {
+        c = 0x7fu;                                   // NaN
+    } else if (a >= 0x43e00000u) {
+        c = 0x7eu;                                   // |f| >= 448: the largest finite value
+    } else if (a < 0x3c800000u) {
+        c = (uint32_t)rintf(__uint_as_float(a) * 512.0f);   // below 2^-6: m * 2^-9, m = 0..8
+    } else {
+        // normal: keep 3 mantissa bits, ties to even; a carry moves into the exponent
+        const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+        c = (r >> 20) - (120u << 3);
+    }
+    return c | ((u >> 24) & 0x80u);
+}
+
+// V >= 4: four elements per word, element 4k in the lowest byte of word k.
+template <int V> struct Cvt<FP8T, V> {
+    static constexpr int n = V;
+    static __device__ __forceinline__ void unpack(const Vec<V>& v, float* f) {
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[k], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[k], true);
+            f[4 * k] = lo[0];
+            f[4 * k + 1] = lo[1];
+            f[4 * k + 2] = hi[0];
+            f[4 * k + 3] = hi[1];
+        }
+    }
+    static __device__ __forceinline__ Vec<V> pack(const float* f) {
+        Vec<V> v;
+#pragma unroll
+        for (int k = 0; k < V / 4; ++k)
+            v.w[k] = fp8_e4m3_rne(f[4 * k]) | (fp8_e4m3_rne(f[4 * k + 1]) << 8) |
+                     (fp8_e4m3_rne(f[4 * k + 2]) << 16) | (fp8_e4m3_rne(f[4 * k + 3]) << 24);
+        return v;
+    }
+};
+template <> struct Cvt<FP8T, 1> {
+    static constexpr int n = 1;
+    static __device__ __forceinline__ void unpack(const Vec<1>& v, float* f) {
+        f[0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.b, false)[0];
+    }
+    static __device__ __forceinline__ Vec<1> pack(const float* f) {
+        Vec<1> v; v.b = (uint8_t)fp8_e4m3_rne(f[0]); return v;
     }
 };
 

@@ -9,7 +9,12 @@
 
 namespace dcp {
 
-enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+// Bytes per payload element of a DType (0 for anything else).
+constexpr int dtype_esize(int dt) {
+    return dt == DT_F32 ? 4 : dt == DT_F16 || dt == DT_BF16 ? 2 : dt == DT_FP8 ? 1 : 0;
+}
 
 // Pack (and the plain strided row copy the N == 1 shortcuts use):
 // for r < R, b < B, h < H with p = h / Hpr, hl = h % Hpr
@@ -96,8 +101,9 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_inplace(const InplaceArgs& a, hipStream_t stream);
 
-// Largest vector width (16, 8, 4 or 2 bytes) such that every row length is a
-// multiple of it and every address used is aligned to min(width, 4).
+// Largest vector width (16, 8, 4, 2 or 1 bytes, at least esize) such that
+// every row length is a multiple of it and every address used is aligned to
+// min(width, 4).
 int pick_vec_bytes(int64_t row_bytes, int esize, const int64_t* addrs_and_strides, int count);
 
 // Launches are split so that one launch never addresses more than this many

@@ -323,7 +323,7 @@ hipError_t run_dt(const InplaceArgs& a, int V, hipStream_t stream) {
 
 hipError_t launch_inplace(const InplaceArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    const int esize = a.dtype == DT_F32 ? 4 : 2;
+    const int esize = dtype_esize(a.dtype);
     int64_t addrs[] = {(int64_t)(uintptr_t)a.partial, a.p_N, a.p_T, a.p_H,
                        (int64_t)(uintptr_t)a.out, a.o_T, a.o_H};
     const int n = a.out ? 7 : 4;
@@ -332,6 +332,7 @@ hipError_t launch_inplace(const InplaceArgs& a, hipStream_t stream) {
     switch (a.dtype) {
         case DT_F32: return run_dt<F32T>(a, V, stream);
         case DT_F16: return run_dt<F16T>(a, V, stream);
+        case DT_FP8: return run_dt<FP8T>(a, V, stream);
         default: return run_dt<BF16T>(a, V, stream);
     }
 }

@@ -105,9 +105,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
 // payload dword j of the block comes from source dword j - k, where k is the
 // row it sits in; a chunk that holds the LSE word of row k takes three
 // payload dwords from source dwords base-1..base+2 and the LSE in between.
-// A wave-step covers 64 chunks (256 dwords); with W >= 1024 bytes it holds at
-// most one LSE word, at a wave-uniform position, so the LSE arrives through a
-// scalar load.
+// A wave-step covers 64 chunks (256 dwords); with W >= 512 bytes it holds at
+// most two LSE words (rows k and k + 1), at wave-uniform positions, so the
+// LSEs arrive through scalar loads.
 // ---------------------------------------------------------------------------
 struct StreamK {
     const char* src;
@@ -121,7 +121,7 @@ struct StreamK {
     uint32_t nsteps;           // R * B * N * S wave-steps in this launch
     uint32_t S;                // wave-steps per block = ceil(Q / 64)
     uint32_t Q;                // 16-byte chunks per block = Hpr * W / 16
-    uint32_t Wd;               // dwords per row incl. the LSE word = W / 4 (>= 256)
+    uint32_t Wd;               // dwords per row incl. the LSE word = W / 4 (>= 128)
     uint32_t Hpr, N, B;
     FastDiv f_S, f_N, f_B, f_Wd;
 };
@@ -143,7 +143,9 @@ constexpr int64_t kStreamWide = 32768;
 // costs 3% (the DeepSeek-V3-shaped pack, 67 MB of source).
 constexpr int64_t kStreamNtSourceBytes = int64_t(96) << 20;
 
-template <int U, int WPB, bool NTL>
+// TWO: rows of 512 to 1020 bytes, where a wave-step can hold a second LSE
+// word; rows of 1 KB and more keep the one-LSE form.
+template <int U, int WPB, bool NTL, bool TWO>
 __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
@@ -161,16 +163,19 @@ __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) 
             const uint32_t p = blk - rb * k.N;
             const uint32_t r = fdiv(rb, k.f_B);
             const uint32_t b = rb - r * k.B;
-            // the LSE word in dwords [256 s, 256 s + 256) of the block, if any:
-            // the first LSE at or after dword d0 belongs to row d0 / Wd
+            // the LSE words in dwords [256 s, 256 s + 256) of the block: the
+            // first LSE at or after dword d0 belongs to row kl = d0 / Wd (at
+            // dword jl >= d0), the next one, Wd dwords later, to row kl + 1
             const uint32_t d0 = s * 256u;
             const uint32_t kl = fdiv(d0, k.f_Wd);
             const uint32_t jl = kl * k.Wd + k.Wd - 1u;
             // a token this rank owns no KV for is sent as the neutral pair
             const bool neutral = k.kv != nullptr && load_word(k.kv + r * k.kv_R + b * k.kv_B) == 0u;
-            uint32_t lval = kNegInfBits;
-            if (!neutral && kl < k.Hpr && jl >= d0 && jl < d0 + 256u)
-                lval = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + kl) * k.sl_H);
+            const char* lrow = k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + kl) * k.sl_H;
+            uint32_t lval = kNegInfBits, lval1 = kNegInfBits;
+            if (!neutral && kl < k.Hpr && jl >= d0 && jl < d0 + 256u) lval = load_word(lrow);
+            if constexpr (TWO)
+                if (!neutral && kl + 1u < k.Hpr && jl + k.Wd < d0 + 256u) lval1 = load_word(lrow + k.sl_H);
             const uint32_t q = s * 64u + lane;
             if (q < k.Q) {
                 const uint32_t j0 = q * 4u;                   // first dword of the chunk
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) 
                     uint32_t o[4];
 #pragma unroll
                     for (int d = 0; d < 4; ++d)
-                        o[d] = (uint32_t)d < t ? x.w[d + 1] : ((uint32_t)d == t ? lval : x.w[d]);
+                        o[d] = (uint32_t)d < t ? x.w[d + 1] : ((uint32_t)d == t ? (TWO && row != kl ? lval1 : lval) : x.w[d]);
 #pragma unroll
                     for (int d = 0; d < 4; ++d) x.w[d] = o[d];
                 }
@@ -202,17 +207,29 @@ __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) 
 
 // True when dst/dst_lse form a peer-outer interleaved buffer whose blocks the
 // stream kernel can write: LSE word right after each payload row, rows
-// contiguous, 16-byte aligned blocks, rows of at least 1 KB, and the source
+// contiguous, 16-byte aligned blocks, rows of at least 512 bytes, and the source
 // head rows contiguous and dword aligned.
 bool stream_layout(const PackArgs& a) {
     if (a.dst == nullptr || a.dst_lse == nullptr || a.Hpr < 1) return false;
     const int64_t W = a.row_bytes + 4;
-    if (a.row_bytes % 4 != 0 || W / 4 < 256) return false;
+    if (a.row_bytes % 4 != 0 || W / 4 < 128) return false;
     if (a.dst_lse != a.dst + a.row_bytes) return false;
     if (a.d_H != W || a.dl_H != W || a.dl_R != a.d_R || a.dl_N != a.d_N || a.dl_B != a.d_B) return false;
     if ((uintptr_t)a.dst % 16 || a.d_R % 16 || a.d_N % 16 || a.d_B % 16 || (a.Hpr * W) % 16) return false;
     if (a.s_H != a.row_bytes || (uintptr_t)a.src % 4 || a.s_R % 4 || a.s_B % 4) return false;
     return true;
+}
+
+template <bool TWO>
+hipError_t launch_stream(const StreamK& k, bool nt_source, hipStream_t stream) {
+    if (k.nsteps >= kStreamWide) {
+        const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
+        if (nt_source)
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO>, dim3(blocks), dim3(512), stream, k);
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO>, dim3(blocks), dim3(512), stream, k);
+    }
+    const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
+    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO>, dim3(blocks), dim3(256), stream, k);
 }
 
 hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
@@ -253,17 +270,8 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.f_N = make_fastdiv(k.N);
             k.f_B = make_fastdiv(k.B);
             k.f_Wd = make_fastdiv(k.Wd);
-            hipError_t e;
-            if (k.nsteps >= kStreamWide) {
-                const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
-                if (nt_source)
-                    e = launch_kernel(pack_stream_kernel<kStreamU, 8, true>, dim3(blocks), dim3(512), stream, k);
-                else
-                    e = launch_kernel(pack_stream_kernel<kStreamU, 8, false>, dim3(blocks), dim3(512), stream, k);
-            } else {
-                const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-                e = launch_kernel(pack_stream_kernel<kStreamU, 4, false>, dim3(blocks), dim3(256), stream, k);
-            }
+            const hipError_t e = k.Wd < 256 ? launch_stream<true>(k, nt_source, stream)
+                                             : launch_stream<false>(k, nt_source, stream);
             if (e != hipSuccess) return e;
         }
     }
@@ -343,7 +351,7 @@ hipError_t run_v(const PackArgs& a, hipStream_t stream) {
 }  // namespace
 
 int pick_vec_bytes(int64_t row_bytes, int esize, const int64_t* addrs, int count) {
-    static const int widths[4] = {16, 8, 4, 2};
+    static const int widths[5] = {16, 8, 4, 2, 1};
     for (int w : widths) {
         if (w < esize) continue;
         if (row_bytes % w != 0) continue;
@@ -368,7 +376,8 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
         case 16: return run_v<16>(a, stream);
         case 8: return run_v<8>(a, stream);
         case 4: return run_v<4>(a, stream);
-        default: return run_v<2>(a, stream);
+        case 2: return run_v<2>(a, stream);
+        default: return run_v<1>(a, stream);
     }
 }
 

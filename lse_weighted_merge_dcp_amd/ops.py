@@ -27,7 +27,8 @@ import torch
 
 from . import _lib
 
-_DTYPE = {torch.float32: _lib.DCP_F32, torch.float16: _lib.DCP_F16, torch.bfloat16: _lib.DCP_BF16}
+_DTYPE = {torch.float32: _lib.DCP_F32, torch.float16: _lib.DCP_F16, torch.bfloat16: _lib.DCP_BF16,
+          torch.float8_e4m3fn: _lib.DCP_FP8_E4M3}
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -66,7 +67,8 @@ def _lse_ok(t: torch.Tensor, name: str) -> None:
 
 def lse_pack_dim(dtype: torch.dtype) -> int:
     """Payload elements one fp32 LSE occupies at the tail of a row: 1 for
-    float32, 2 for float16/bfloat16.  Other dtypes raise ValueError."""
+    float32, 2 for float16/bfloat16, 4 for float8_e4m3fn.  Other dtypes raise
+    ValueError."""
     code = _lib.lib().dcp_lse_pack_dim(_DTYPE.get(dtype, -1))
     if code < 0:
         raise ValueError("no LSE pack dim for dtype %s" % dtype)

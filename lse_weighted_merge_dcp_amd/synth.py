@@ -29,14 +29,17 @@ stand in for them):
                 sqrt(e^(ln2^2) - 1)/sqrt(L) = 0.785/sqrt(L), i.e. 1.1325/sqrt(L)
                 in log2 units), drawn directly because exact draws would take
                 3.4e10 samples at B = 512.
+  6 "dsv3fp8"   the shape of 2 with an OCP FP8 E4M3 payload (out ~ N(0,1)
+                rounded to fp8), base-2 LSE from the law of 5 over
+                L ~ U{1024..16384}.
 
 N(a, b) means mean a, standard deviation b.  Every draw comes from a
 generator seeded by (seed, workload, rank, stream), so any rank's data can be
 regenerated on its own and the result does not depend on thread counts.
 
-Payload arrays are numpy arrays in the storage type: float32, float16, or
-uint16 holding bf16 bits (bf16 values are float32 draws rounded to nearest
-even by torch's conversion).
+Payload arrays are numpy arrays in the storage type: float32, float16,
+uint16 holding bf16 bits, or uint8 holding fp8 codes (bf16 and fp8 values
+are float32 draws rounded to nearest even by torch's conversion).
 """
 from __future__ import annotations
 
@@ -46,7 +49,10 @@ import math
 import numpy as np
 import torch
 
-ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+# numpy storage of each payload type: bf16 as raw uint16 bits, fp8 (OCP E4M3)
+# as raw uint8 codes
+NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 LONGCTX_BATCHES = (1, 8, 64, 256, 512)
 
 
@@ -58,7 +64,7 @@ class Workload:
     B: int          # tokens (T for the in-place workload)
     H: int
     D: int
-    dtype: str      # "f32" | "f16" | "bf16"
+    dtype: str      # "f32" | "f16" | "bf16" | "fp8"
     base2: bool
     layout: str     # "interleaved" | "split" | "inplace"
     seed: int
@@ -86,6 +92,8 @@ WORKLOADS = {
     "kimi": Workload("kimi", 4, N=8, B=16384, H=96, D=512, dtype="f32", base2=False, layout="inplace", seed=3),
     "longctx": Workload("longctx", 5, N=16, B=512, H=128, D=512, dtype="bf16", base2=True,
                         layout="interleaved", seed=4),
+    "dsv3fp8": Workload("dsv3fp8", 6, N=8, B=64, H=128, D=512, dtype="fp8", base2=True, layout="interleaved",
+                        seed=5),
 }
 
 
@@ -109,6 +117,8 @@ def to_storage(x: torch.Tensor, dtype: str) -> np.ndarray:
         return x.to(torch.float16).numpy()
     if dtype == "bf16":
         return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if dtype == "fp8":
+        return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     raise ValueError(dtype)
 
 
@@ -123,7 +133,7 @@ def rank_inputs(w: Workload):
     kv_len=[N,B] int64 or None).
     """
     N, B, H, D = w.N, w.B, w.H, w.D
-    out = np.empty((N, B, H, D), {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype])
+    out = np.empty((N, B, H, D), NP_STORAGE[w.dtype])
     lse = np.empty((N, B, H), np.float32)
     kv_len = None
     if w.key == "tiny":
@@ -145,6 +155,16 @@ def rank_inputs(w: Workload):
             for b in range(B):
                 s = torch.randn(H, int(kv_len[r, b]), generator=g)
                 lse[r, b] = torch.log2(torch.exp2(s).sum(dim=1, dtype=torch.float64)).to(torch.float32).numpy()
+    elif w.key == "dsv3fp8":
+        # the DeepSeek-V3 shape with an fp8 payload; LSEs from the large-L law
+        # of the long-context recipe over L ~ U{1024..16384}
+        kv_len = np.empty((N, B), np.int64)
+        for r in range(N):
+            out[r] = _normal_rows(w, r, (B, H, D))
+            kv_len[r] = np_rng(w, r, 1).integers(1024, 16384, size=B, endpoint=True)
+            z = np_rng(w, r, 2).normal(0.0, 1.0, size=(B, H))
+            L = kv_len[r].astype(np.float64)[:, None]
+            lse[r] = np.log2(L) + math.log(2.0) / 2.0 + 1.1325 * z / np.sqrt(L)
     elif w.key == "split":
         for r in range(N):
             out[r] = _normal_rows(w, r, (B, H, D))

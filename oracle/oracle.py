@@ -9,10 +9,11 @@ The arithmetic lives in ``dcp_oracle.c`` (plain fp64 loops).  This wrapper
 only moves numpy arrays in and out:
 
 * payload arrays are numpy views of any strides; dtype tags are ``"f32"``,
-  ``"f16"`` and ``"bf16"`` (bf16 is carried as raw ``uint16`` bits);
+  ``"f16"``, ``"bf16"`` (carried as raw ``uint16`` bits) and ``"fp8"`` (OCP
+  FP8 E4M3, carried as raw ``uint8`` codes);
 * LSE arrays are ``float32`` views of any strides;
 * the combine and in-place functions decode the payload to fp64 exactly
-  (every fp32/fp16/bf16 value is an fp64 value) before calling C.
+  (every fp32/fp16/bf16/fp8 value is an fp64 value) before calling C.
 
 Citations (page title, then section):
   sglang PR #34651 report -- 实现拆解 items 1-3 and its split-layout test excerpt;
@@ -23,6 +24,7 @@ Citations (page title, then section):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -33,7 +35,7 @@ _SRC = os.path.join(_HERE, "dcp_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libdcp_oracle.so")
 _lib = None
 
-ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+ESIZE = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 
 def compile_source(src: str, out: str) -> str:
@@ -100,8 +102,28 @@ def _ptr(a: np.ndarray) -> int:
 # --------------------------------------------------------------------------
 # exact decoding of the payload element types to fp64
 # --------------------------------------------------------------------------
+def fp8_e4m3_values() -> np.ndarray:
+    """fp64 value of each of the 256 codes of OCP FP8 E4M3 (e4m3fn), from the
+    format's definition: bit 7 the sign, bits 6..3 the exponent e (bias 7),
+    bits 2..0 the mantissa m; e = 0 encodes the subnormals (m / 8) * 2^-6,
+    e = 15 with m = 7 is NaN, and there are no infinities (so e = 15, m < 7
+    are ordinary numbers, the largest 1.75 * 2^8 = 448)."""
+    t = np.empty(256, np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 0xF and m == 0x7:
+            t[c] = math.nan
+        elif e == 0:
+            t[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            t[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
 def to_f64(a: np.ndarray, dt: str) -> np.ndarray:
-    """Exact fp64 value of every element (bf16 given as raw uint16 bits)."""
+    """Exact fp64 value of every element (bf16 given as raw uint16 bits,
+    fp8 as raw uint8 codes)."""
     if dt == "f32":
         assert a.dtype == np.float32
         return a.astype(np.float64)
@@ -112,6 +134,9 @@ def to_f64(a: np.ndarray, dt: str) -> np.ndarray:
         assert a.dtype == np.uint16
         # a bf16 value is the fp32 value whose upper 16 bits are these bits
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dt == "fp8":
+        assert a.dtype == np.uint8
+        return fp8_e4m3_values()[a]
     raise ValueError(dt)
 
 

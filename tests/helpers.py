@@ -4,8 +4,10 @@ the acceptance checks against the oracle.
 Tolerances (the bar stated for this path):
   combine / in-place outputs:  |got - ref| <= tau_T * M + floor_T, with
       M = sum_i w_i |nan_to_num(o_i)| (fp64, from the oracle) and tau_T =
-      1e-5 (fp32), 2^-7 (bf16), 2^-10 (fp16); floor_T is half the spacing of
-      T's subnormals (output rounding of tiny values).  M == 0 requires got == 0.
+      1e-5 (fp32), 2^-7 (bf16), 2^-10 (fp16), 2^-4 + 2^-18 (OCP FP8 E4M3:
+      half an fp8 ulp, 2^-4 of |out| <= M, plus the fp32 accumulation of up to
+      ~60 terms); floor_T is half the spacing of T's subnormals (output
+      rounding of tiny values).  M == 0 requires got == 0.
   scaled partials (in-place):  |got - ref| <= tau_T * |ref| + floor_T.
   global LSE:  same class (NaN / +inf / -inf) when the reference is not
       finite; otherwise |got - ref| <= 1e-5 + ulp_fp32(ref): 1e-5 absolute
@@ -18,24 +20,29 @@ import math
 import numpy as np
 import torch
 
-TAU = {"f32": 1e-5, "bf16": 2.0 ** -7, "f16": 2.0 ** -10}
-FLOOR = {"f32": 2.0 ** -150, "bf16": 2.0 ** -134, "f16": 2.0 ** -25}
-TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-NP_DT = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+TAU = {"f32": 1e-5, "bf16": 2.0 ** -7, "f16": 2.0 ** -10, "fp8": 2.0 ** -4 + 2.0 ** -18}
+FLOOR = {"f32": 2.0 ** -150, "bf16": 2.0 ** -134, "f16": 2.0 ** -25, "fp8": 2.0 ** -10}
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+NP_DT = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 def to_dev(a: np.ndarray, dt: str, dev) -> torch.Tensor:
-    """Storage array (bf16 as uint16 bits) -> device tensor of the payload type."""
+    """Storage array (bf16 as uint16 bits, fp8 as uint8 codes) -> device
+    tensor of the payload type."""
     if dt == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    if dt == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(torch.float8_e4m3fn)
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
 def to_host(t: torch.Tensor, dt: str) -> np.ndarray:
-    """Device tensor -> storage array (bf16 as uint16 bits)."""
+    """Device tensor -> storage array (bf16 as uint16 bits, fp8 as uint8 codes)."""
     t = t.detach().cpu()
     if dt == "bf16":
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if dt == "fp8":
+        return t.contiguous().view(torch.uint8).numpy()
     return t.contiguous().numpy()
 
 
@@ -46,6 +53,8 @@ def bytes_of(t: torch.Tensor) -> np.ndarray:
 def decode(a: np.ndarray, dt: str) -> np.ndarray:
     if dt == "bf16":
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dt == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     return a.astype(np.float64)
 
 

@@ -58,13 +58,17 @@ def test_lse_pack_dim_and_status_strings():
     assert lib.dcp_lse_pack_dim(0) == 1
     assert lib.dcp_lse_pack_dim(1) == 2
     assert lib.dcp_lse_pack_dim(2) == 2
-    assert lib.dcp_lse_pack_dim(3) == DTYPE
+    assert lib.dcp_lse_pack_dim(3) == 4          # OCP FP8 E4M3: 4 bytes / 1 byte
+    assert lib.dcp_lse_pack_dim(4) == DTYPE
     assert lib.dcp_lse_pack_dim(-1) == DTYPE
     for code, name in _lib.STATUS.items():
         assert lib.dcp_status_str(code).decode().startswith(name)
     assert ops.lse_pack_dim(torch.float16) == 2
+    assert ops.lse_pack_dim(torch.float8_e4m3fn) == 4
     with pytest.raises(ValueError):
         ops.lse_pack_dim(torch.float64)
+    with pytest.raises(ValueError):
+        ops.lse_pack_dim(torch.float8_e5m2)
 
 
 def pack(**kw):
@@ -93,13 +97,15 @@ def inplace(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(dtype=4), DTYPE), (dict(dtype=-1), DTYPE),
     (dict(N=0), SHAPE), (dict(H=0), SHAPE), (dict(D=0), SHAPE), (dict(B=-1), SHAPE), (dict(R=-1), SHAPE),
     (dict(N=3), HEADS), (dict(N=16), HEADS),
     (dict(so_H=-1), STRIDE), (dict(dl_N=-4), STRIDE), (dict(do_R=-1), STRIDE),
     (dict(src_o=None), NULL), (dict(dst_lse=None), NULL),
     (dict(src_lse=A + 2), ALIGN), (dict(dst_o=A + 1, dtype=1), ALIGN), (dict(dst_o=A + 2, dtype=0), ALIGN),
     (dict(kv_len=A + 2), ALIGN), (dict(kl_B=-1), STRIDE), (dict(kv_len=A, B=0), OK),
+    (dict(dst_o=A + 1, dtype=3, B=0), OK), (dict(dst_lse=A + 1, dtype=3), ALIGN),   # fp8: byte-aligned payload
+    (dict(D=1 << 28, dtype=3), SHAPE),
     (dict(H=1 << 25, N=1), SHAPE), (dict(D=1 << 27), SHAPE),
     (dict(H=1 << 22, N=1), SHAPE), (dict(H=1 << 11, N=1, D=1 << 20), SHAPE),   # one token's rows > 2^25
     (dict(B=0), OK), (dict(R=0), OK), (dict(B=0, src_o=None), OK),
@@ -150,6 +156,14 @@ def test_binding_rejects_host_tensors_and_bad_layouts():
     assert words.stride() == (2 * 4 * 33, 4 * 33, 33)
     with pytest.raises(ValueError):
         ops.interleaved_views(torch.zeros(2, 2, 4, 65, dtype=torch.bfloat16), 63)
+    # fp8: an interleaved row is D + 4 bytes, the LSE is fp32 word D / 4
+    send = torch.zeros(2, 2, 4, 68, dtype=torch.float8_e4m3fn)
+    pay, words = ops.interleaved_views(send, 64)
+    assert pay.shape == (2, 2, 4, 64) and words.shape == (2, 2, 4)
+    assert words.stride() == (2 * 4 * 17, 4 * 17, 17)
+    assert words.data_ptr() == send.data_ptr() + 64
+    with pytest.raises(ValueError):
+        ops.interleaved_views(torch.zeros(2, 2, 4, 66, dtype=torch.float8_e4m3fn), 62)
     # empty buffers: any strides (numpy gives zero-size arrays zero strides)
     import numpy as np
     empty = torch.from_numpy(np.zeros((2, 0, 4, 66), np.float16))

@@ -50,7 +50,7 @@ def check_destinations(w, pay, words, got_out, got_g):
             check_lse(got_g[p].cpu().numpy(), g)
 
 
-INTERLEAVED = [("tiny", None), ("dsv3", None)] + [("longctx", b) for b in synth.LONGCTX_BATCHES]
+INTERLEAVED = [("tiny", None), ("dsv3", None), ("dsv3fp8", None)] + [("longctx", b) for b in synth.LONGCTX_BATCHES]
 
 
 @pytest.mark.parametrize("key,B", INTERLEAVED)
@@ -85,7 +85,7 @@ def test_combine_split_workload():
         check_lse(g[p].cpu().numpy(), gr)
 
 
-@pytest.mark.parametrize("key,B", [("tiny", None), ("dsv3", None), ("longctx", 64), ("split", None)])
+@pytest.mark.parametrize("key,B", [("tiny", None), ("dsv3", None), ("longctx", 64), ("split", None), ("dsv3fp8", None)])
 def test_end_to_end_pack_exchange_combine(key, B):
     w, inp = inputs(key, B)
     say("end to end", w.describe())
@@ -110,7 +110,7 @@ def test_end_to_end_pack_exchange_combine(key, B):
 SPECIALS = [math.nan, math.inf, -math.inf, -2.5, 0.0, 7.25]
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16", "fp8"])
 @pytest.mark.parametrize("base2", [False, True])
 def test_special_values_every_combination(dt, base2):
     """Every combination of special LSE values over N=3 peers, with NaN and
@@ -131,7 +131,7 @@ def test_special_values_every_combination(dt, base2):
     check_lse(gg.cpu().numpy(), gr)
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16", "fp8"])
 @pytest.mark.parametrize("N", [1, 2, 3, 5, 8, 16, 17, 33])
 @pytest.mark.parametrize("D", [64, 100, 512])
 def test_general_shapes(dt, N, D):
@@ -159,7 +159,8 @@ def test_general_shapes(dt, N, D):
             check_lse(gg[r].cpu().numpy(), gr)
 
 
-@pytest.mark.parametrize("dt,N,D", [("bf16", 8, 400), ("f16", 16, 384), ("f32", 4, 1000), ("bf16", 2, 512)])
+@pytest.mark.parametrize("dt,N,D", [("bf16", 8, 400), ("f16", 16, 384), ("f32", 4, 1000), ("bf16", 2, 512),
+                                    ("fp8", 8, 1024), ("fp8", 16, 800)])
 @pytest.mark.parametrize("B", [5, 300])
 def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
     """Rows of 768 bytes and more take the row-per-wave kernel: at B = 5 in
@@ -195,6 +196,8 @@ def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
     ("f32", 17, 4, 3, 64),       # any-N path
     ("bf16", 3, 4, 2, 100),      # element-granular rows
     ("f32", 1, 4, 3, 64),        # N = 1 copy onto itself
+    ("fp8", 8, 5, 4, 1024),      # fp8, row-per-wave kernel
+    ("fp8", 4, 9, 5, 128),       # fp8, short-row kernel
 ])
 def test_out_may_alias_peer_zero(dt, N, B, Hpr, D):
     """out may be exactly recv_o's peer 0 rows: the merge lands in place in

@@ -45,7 +45,7 @@ def test_inplace_kimi_shape_small_T(T):
     check_scaled(part.cpu().numpy(), scaled, "f32")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16", "fp8"])
 @pytest.mark.parametrize("N,P,rank0", [(8, 8, 0), (4, 1, 2), (8, 3, 5), (3, 3, 0), (17, 17, 0), (17, 2, 7), (2, 2, 0), (16, 16, 0)])
 def test_inplace_held_subsets_and_dtypes(dt, N, P, rank0):
     """P of the N ranks' partials held (rank0 .. rank0+P-1): the single-rank
@@ -70,7 +70,7 @@ def test_inplace_held_subsets_and_dtypes(dt, N, P, rank0):
 
 
 @pytest.mark.parametrize("dt,D", [("f32", 512), ("f32", 520), ("f32", 192), ("bf16", 100), ("f16", 512),
-                                  ("bf16", 1000)])
+                                  ("bf16", 1000), ("fp8", 2048), ("fp8", 100)])
 @pytest.mark.parametrize("want_out", [True, False])
 def test_inplace_single_rank_segment_groups(dt, D, want_out):
     """P = 1, one rank scaling its own partial: each row group takes two

@@ -47,7 +47,7 @@ def host_view(host, npdt, shape):
     return host[GUARD:GUARD + n].view(npdt).reshape(shape)
 
 
-INTERLEAVED = [("tiny", None), ("dsv3", None)] + [("longctx", b) for b in synth.LONGCTX_BATCHES]
+INTERLEAVED = [("tiny", None), ("dsv3", None), ("dsv3fp8", None)] + [("longctx", b) for b in synth.LONGCTX_BATCHES]
 
 
 @pytest.mark.parametrize("key,B", INTERLEAVED)
@@ -80,7 +80,14 @@ STREAM_SHAPES = [
     ("f16", 2, 3, 8, 1024),     # 2 KB fp16 rows
     ("bf16", 1, 4, 8, 768),     # a single peer (N = 1)
     ("bf16", 2, 3, 3, 512),     # Hpr * W not a multiple of 16: falls back to the row kernel
-    ("bf16", 2, 3, 8, 504),     # rows under 1 KB: row kernel
+    ("bf16", 2, 3, 8, 504),     # rows just under 1 KB (W = 1012): two LSE words in some wave-steps
+    ("bf16", 4, 3, 8, 256),     # W = 516: two LSE words in most wave-steps
+    ("f32", 2, 5, 8, 127),      # W = 512 (128 dwords, the smallest stream row)
+    ("bf16", 2, 3, 4, 382),     # W = 768
+    ("bf16", 2, 3, 8, 200),     # rows under 512 B (W = 404): row kernel
+    ("fp8", 8, 5, 16, 512),     # the fp8 decode shape (W = 516, lpd = 4)
+    ("fp8", 8, 5, 16, 1024),    # fp8 rows of 1 KB (W = 1028)
+    ("fp8", 4, 3, 8, 2044),     # fp8 rows of 2 KB
 ]
 
 
@@ -109,7 +116,8 @@ def test_pack_interleaved_stream_shapes(dt, N, B, Hpr, D):
     assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
 
 
-SPLIT = [("f16", 4, 256, 16, 128), ("bf16", 2, 4, 8, 128), ("bf16", 4, 1, 16, 512), ("f32", 8, 3, 2, 64)]
+SPLIT = [("f16", 4, 256, 16, 128), ("bf16", 2, 4, 8, 128), ("bf16", 4, 1, 16, 512), ("f32", 8, 3, 2, 64),
+         ("fp8", 4, 8, 16, 128)]
 
 
 @pytest.mark.parametrize("dt,N,B,Hpr,D", SPLIT)
@@ -147,6 +155,9 @@ def test_pack_split_peer_inside(dt, N, B, Hpr, D):
     ("f32", 4, 3, 8, 5, 1, 3),      # 20-byte rows: 4-byte accesses
     ("bf16", 4, 9, 8, 72, 0, 0),    # 144-byte rows: 16-byte accesses, ragged row groups
     ("f32", 2, 2, 2, 1024, 0, 0),   # 4 KiB rows: several steps per row
+    ("fp8", 2, 5, 6, 7, 1, 3),      # fp8: 7-byte rows at odd byte offsets: 1-byte accesses
+    ("fp8", 3, 4, 9, 14, 0, 2),     # fp8: 14-byte rows, 2-byte aligned: 2-byte accesses
+    ("fp8", 4, 9, 8, 144, 0, 0),    # fp8: 144-byte rows: 16-byte accesses
 ])
 def test_pack_odd_shapes_and_offsets(dt, N, B, H, D, src_off, dst_off):
     say("pack odd", dt, N, B, H, D, src_off, dst_off)

@@ -265,6 +265,26 @@ def test_decoders_exact():
     np.testing.assert_array_equal(orc.to_f64(bits, "bf16"), bf.to(torch.float64).numpy())
 
 
+def test_fp8_decoder_against_torch_and_hand_values():
+    """OCP FP8 E4M3: every one of the 256 codes decodes as torch's
+    float8_e4m3fn does (NaN where torch has NaN), and a few codes worked by
+    hand from the format: 0x38 = 1, 0x7E = 448 (largest), 0x08 = 2^-6
+    (smallest normal), 0x01 = 2^-9 (smallest subnormal), 0x80 = -0, 0xFE =
+    -448, 0x70 = 2^(14-7) = 128, 0x7F and 0xFF NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.to_f64(codes, "fp8")
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    np.testing.assert_array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    hand = {0x38: 1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x00: 0.0, 0xFE: -448.0,
+            0x70: 128.0, 0x3C: 1.5, 0xB8: -1.0, 0x07: 7 * 2.0 ** -9}
+    for c, v in hand.items():
+        assert got[c] == v, hex(c)
+    assert math.copysign(1.0, got[0x80]) == -1.0 and got[0x80] == 0.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.isnan(got).sum() == 2 and not np.isinf(got).any()
+
+
 # --------------------------------------------------------------------------
 # in-place merge: consistent with the combine, the brute force and the slice
 # --------------------------------------------------------------------------
