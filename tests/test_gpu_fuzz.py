@@ -27,9 +27,9 @@ from helpers import NP_DT, TORCH_DT, check_lse, check_out, check_scaled, decode,
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-SETTINGS = dict(max_examples=40, derandomize=True, deadline=None, print_blob=True,
+SETTINGS = dict(max_examples=48, derandomize=True, deadline=None, print_blob=True,
                 suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
-DTS = ["f32", "f16", "bf16"]
+DTS = ["f32", "f16", "bf16", "fp8"]
 SPECIAL = np.array([np.nan, np.inf, -np.inf], np.float32)
 
 
@@ -63,6 +63,8 @@ class Buf:
         h = self.host
         if self.np_dt == np.uint16:
             self.dev = torch.from_numpy(h.view(np.int16)).to(DEV).view(torch.bfloat16)
+        elif self.np_dt == np.uint8 and self.torch_dt == torch.float8_e4m3fn:
+            self.dev = torch.from_numpy(h).to(DEV).view(torch.float8_e4m3fn)
         else:
             self.dev = torch.from_numpy(h).to(DEV)
         return self
@@ -74,6 +76,8 @@ class Buf:
         t = self.dev.cpu()
         if self.np_dt == np.uint16:
             return t.view(torch.int16).numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
         return t.numpy()
 
 
@@ -97,6 +101,8 @@ def fill_payload(rng, buf, dt, specials):
         r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)     # round to nearest even
         r[np.isnan(x)] = 0x7FC0
         v[...] = r
+    elif dt == "fp8":
+        v[...] = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()   # inf becomes NaN
     else:
         v[...] = x.astype(NP_DT[dt])
 
@@ -150,13 +156,14 @@ def test_fuzz_pack(data):
         send = np.frombuffer(rng.bytes(R * N * B * Hpr * (D + lpd) * np.dtype(NP_DT[dt]).itemsize),
                              NP_DT[dt]).reshape(R, N, B, Hpr, D + lpd).copy()
         d_send = torch.from_numpy(send.view(np.int16) if dt == "bf16" else send).to(DEV)
-        if dt == "bf16":
-            d_send = d_send.view(torch.bfloat16)
+        if dt in ("bf16", "fp8"):
+            d_send = d_send.view(TORCH_DT[dt])
         d_pay, d_words = ops.interleaved_views(d_send, D)
         ops.dcp_pack_a2a_send(src.upload().dview(), lse.upload().dview(), d_pay, d_words,
                               kv_len=torch.from_numpy(kv).to(DEV) if use_kv else None)
         got = d_send.cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else got.numpy()
+        got = got.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else got.view(torch.uint8).numpy() \
+            if dt == "fp8" else got.numpy()
         want = send.copy()
         h_pay, h_words = orc.interleaved_views_np(want, D, dt)
         for r in range(R):
