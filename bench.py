@@ -151,7 +151,6 @@ class A2AWorkload:
         nb = algorithmic_bytes(key, B)
         self.bytes_pack, self.bytes_combine = nb["pack"], nb["combine"]
         self.bytes_layer = self.bytes_pack + self.bytes_combine
-        self.dtype = w.dtype
 
     def pack(self, l):
         k = l % self.distinct
@@ -213,7 +212,8 @@ class A2AWorkload:
                                  "dsv3fp8": "DeepSeek-V3-shaped MLA decode, fp8 payload"}[w.key],
                                 w.N, w.B, w.H, w.Hpr, w.D, w.dtype, "2" if w.base2 else "e", w.layout,
                                 self.layers),
-                "N": w.N, "B": w.B, "H": w.H, "D": w.D, "layers": self.layers, "layout": w.layout,
+                "N": w.N, "B": w.B, "H": w.H, "D": w.D, "payload_dtype": w.dtype, "layers": self.layers,
+                "layout": w.layout,
                 "distinct_buffer_sets": self.distinct}
 
     def cpu_sample(self, budget_s):
@@ -268,7 +268,6 @@ class InplaceWorkload:
         torch.cuda.synchronize()
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
         self.bytes_call = algorithmic_bytes("kimi", B)["inplace"]
-        self.dtype = "f32"
 
     def run(self):
         from lse_weighted_merge_dcp_amd import ops
@@ -305,7 +304,7 @@ class InplaceWorkload:
         w = self.w
         return {"workload": "Kimi-K3-shaped cached-extend in-place merge: N=8 ranks' partials [%d, %d, %d] fp32, "
                             "base-e LSE with 0.1%% NaN/inf" % (w.B, w.H, w.D),
-                "N": w.N, "T": w.B, "H": w.H, "D": w.D}
+                "N": w.N, "T": w.B, "H": w.H, "D": w.D, "payload_dtype": "f32"}
 
     def cpu_sample(self, budget_s):
         import numpy as np
@@ -353,7 +352,6 @@ class ReduceScatterWorkload:
         torch.cuda.synchronize()
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
         self.bytes_call = algorithmic_bytes("kimi-rs", B)["combine"]
-        self.dtype = "f32"
 
     def run(self):
         from lse_weighted_merge_dcp_amd import sim
@@ -396,7 +394,7 @@ class ReduceScatterWorkload:
         return {"workload": "Kimi-K3-shaped cached-extend merge, reduce-scatter flavour: N=8 ranks' partials "
                             "[%d, %d, %d] fp32, base-e LSE with 0.1%% NaN/inf, each rank's %d-head slice of the "
                             "output, no partial write-back" % (w.B, w.H, w.D, w.H // w.N),
-                "N": w.N, "T": w.B, "H": w.H, "D": w.D}
+                "N": w.N, "T": w.B, "H": w.H, "D": w.D, "payload_dtype": "f32"}
 
     def cpu_sample(self, budget_s):
         from oracle import oracle as orc
@@ -744,7 +742,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        # the type the path computes in: LSE arithmetic and accumulation are fp32
+        # for every payload type (the pack is a bit copy); the payload type
+        # itself is config.payload_dtype
+        "dtype": "f32",
         "data": "synthetic",
         "config": wl.config(),
         "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
