@@ -148,3 +148,43 @@ def test_mutant_is_caught(tmp_path, name):
     lib = _build_variant(tmp_path, name, text.replace(old, new, 1))
     failed = pin_suite(lib)
     assert failed, "planted mistake %r passed every pin" % name
+
+
+# --------------------------------------------------------------------------
+# the fp8 (OCP E4M3) decoder of oracle/oracle.py: textual mutants of its
+# source must fail its pin (torch's float8_e4m3fn over all 256 codes)
+# --------------------------------------------------------------------------
+FP8_MUTANTS = {
+    "bias_8": ("2.0 ** (e - 7)", "2.0 ** (e - 8)"),
+    "subnormal_scale": ("(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7"),
+    "ieee_top_exponent": ("if e == 0xF and m == 0x7:", "if e == 0xF:"),
+    "sign_dropped": ("sign = -1.0 if c & 0x80 else 1.0", "sign = 1.0"),
+    "no_implicit_one": ("(1.0 + m / 8.0)", "(m / 8.0)"),
+    "four_mantissa_bits": ("e, m = (c >> 3) & 0xF, c & 0x7", "e, m = (c >> 4) & 0x7, c & 0xF"),
+}
+
+
+def _fp8_pin_holds(values) -> bool:
+    codes = np.arange(256, dtype=np.uint8)
+    got = values()
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    if not np.array_equal(np.isnan(got), np.isnan(want)):
+        return False
+    return bool(np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)]))
+
+
+def test_fp8_decoder_unmodified_passes_its_pin():
+    assert _fp8_pin_holds(orc.fp8_e4m3_values)
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_decoder_mutant_fails_its_pin(name):
+    import inspect
+    import textwrap
+
+    src = textwrap.dedent(inspect.getsource(orc.fp8_e4m3_values))
+    old, new = FP8_MUTANTS[name]
+    assert src.count(old) == 1, name
+    ns = {"np": np, "math": math}
+    exec(src.replace(old, new), ns)
+    assert not _fp8_pin_holds(ns["fp8_e4m3_values"]), name
