@@ -23,6 +23,12 @@ def test_graph_replays_match_eager():
     stk = [sim.StackedInterleaved(w.N, w.B, w.H, w.D, torch.bfloat16, DEV) for _ in range(L)]
     outs = [torch.empty((w.N, w.B, w.Hpr, w.D), dtype=torch.bfloat16, device=DEV) for _ in range(L)]
     gl = [torch.empty((w.N, w.B, w.Hpr), dtype=torch.float32, device=DEV) for _ in range(L)]
+    w8 = synth.WORKLOADS["dsv3fp8"].with_batch(4)          # an fp8 layer in the same step
+    inp8 = synth.rank_inputs(w8)
+    src8 = to_dev(inp8["out"], w8.dtype, DEV)
+    lse8 = torch.from_numpy(inp8["lse"]).to(DEV)
+    stk8 = sim.StackedInterleaved(w8.N, w8.B, w8.H, w8.D, torch.float8_e4m3fn, DEV)
+    out8 = torch.empty((w8.N, w8.B, w8.Hpr, w8.D), dtype=torch.float8_e4m3fn, device=DEV)
     part = torch.randn(8, 16, 12, 128, device=DEV)
     plse = torch.randn(8, 16, 12, device=DEV)
     pcopy = part.clone()
@@ -32,6 +38,8 @@ def test_graph_replays_match_eager():
         for l in range(L):
             stk[l].pack(src[l], lse[l])
             stk[l].combine(is_lse_base_on_e=False, out=outs[l], out_lse=gl[l])
+        stk8.pack(src8, lse8)
+        stk8.combine(is_lse_base_on_e=False, out=out8)
         ops.cp_lse_combine_inplace(part, plse, out=pout)
 
     s = torch.cuda.Stream()
@@ -40,7 +48,7 @@ def test_graph_replays_match_eager():
         step()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    ref = [o.clone() for o in outs] + [g.clone() for g in gl] + [pout.clone(), part.clone()]
+    ref = [o.clone() for o in outs] + [g.clone() for g in gl] + [pout.clone(), part.clone(), out8.view(torch.uint8).clone()]
     g = torch.cuda.CUDAGraph()
     for o in outs:
         o.zero_()
@@ -51,10 +59,11 @@ def test_graph_replays_match_eager():
         for o in outs:
             o.fill_(7.0)
         pout.zero_()
+        out8.view(torch.uint8).fill_(0x38)
         part.copy_(pcopy)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = outs + gl + [pout, part]
+        got = outs + gl + [pout, part, out8]
         for a, b in zip(got, ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "replay %d differs" % rep

@@ -32,12 +32,15 @@ def test_concurrent_streams_match_sequential():
     say("two streams")
     a = layer_inputs("longctx", 64, 0.0)
     b = layer_inputs("longctx", 8, 1.5)
+    c = layer_inputs("dsv3fp8", 16, 0.5)     # an fp8 layer behind b on the second stream
     run_layer(*a)
     run_layer(*b)
+    run_layer(*c)
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (a[3].send, a[4], a[5], b[3].send, b[4], b[5])]
-    for t in (a[3].send, a[4], a[5], b[3].send, b[4], b[5]):
-        t.zero_()
+    bufs = [x[i] if i != 3 else x[3].send for x in (a, b, c) for i in (3, 4, 5)]
+    ref = [t.clone() for t in bufs]
+    for t in bufs:
+        t.view(torch.uint8).zero_()
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     for rep in range(3):
@@ -45,7 +48,8 @@ def test_concurrent_streams_match_sequential():
             run_layer(*a)
         with torch.cuda.stream(s2):
             run_layer(*b)
+            run_layer(*c)
         torch.cuda.synchronize()
-        got = [a[3].send, a[4], a[5], b[3].send, b[4], b[5]]
+        got = bufs
         for x, y in zip(got, ref):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), "concurrent run %d differs" % rep
