@@ -45,3 +45,15 @@ def test_algorithmic_bytes_per_layer():
 def test_percentiles():
     p = bench.percentiles([5.0, 1.0, 3.0, 2.0, 4.0, 6.0, 7.0, 8.0, 9.0, 10.0, 11.0])
     assert p == {"p10": 2.0, "p50": 6.0, "p90": 10.0}
+
+
+def test_fp8_bytes_and_counter_keys():
+    """The fp8 decode layer: rows of D + 4 bytes (lpd = 4).  Counter
+    summaries are kept per workload, and per batch size for the long-context
+    sweep (its default batch is 512)."""
+    b = bench.algorithmic_bytes("dsv3fp8")
+    assert b["pack"] + b["combine"] == 64 * 128 * (3 * 8 + 1) * (512 + 4) == 105_676_800
+    assert b["pack"] == 2 * 8 * 64 * 128 * 516 and b["combine"] == 9 * 64 * 128 * 516
+    assert bench.counter_key("dsv3") == "dsv3" and bench.counter_key("kimi-rs") == "kimi-rs"
+    assert bench.counter_key("longctx", 64) == "longctx_B64"
+    assert bench.counter_key("longctx") == "longctx_B512"
