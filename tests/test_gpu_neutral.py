@@ -29,6 +29,8 @@ DEV = torch.device("cuda:0")
     ("bf16", 16, 40, 8, 512, "interleaved"),  # stream kernel, 8-wave workgroups (>= 32768 wave-steps)
     ("f32", 2, 7, 4, 64, "interleaved"),      # row kernel (short rows)
     ("f16", 4, 6, 16, 128, "split"),          # split layout
+    ("fp8", 8, 9, 16, 512, "interleaved"),    # fp8: two-LSE stream kernel (516-byte rows)
+    ("fp8", 4, 6, 16, 128, "split"),          # fp8 split layout
 ])
 def test_pack_neutralises_zero_kv_tokens(dt, N, B, Hpr, D, layout):
     say("pack kv_len", dt, N, B, Hpr, D, layout)
