@@ -107,7 +107,10 @@ def fp8_e4m3_values() -> np.ndarray:
     format's definition: bit 7 the sign, bits 6..3 the exponent e (bias 7),
     bits 2..0 the mantissa m; e = 0 encodes the subnormals (m / 8) * 2^-6,
     e = 15 with m = 7 is NaN, and there are no infinities (so e = 15, m < 7
-    are ordinary numbers, the largest 1.75 * 2^8 = 448)."""
+    are ordinary numbers, the largest 1.75 * 2^8 = 448).  The pages name fp8
+    only as a payload type still to be reviewed (sglang PR #34651 report,
+    风险与影响; vLLM PR #41160 report, 风险与影响); the format itself is the
+    OCP 8-bit floating-point specification's E4M3."""
     t = np.empty(256, np.float64)
     for c in range(256):
         sign = -1.0 if c & 0x80 else 1.0
