@@ -440,3 +440,20 @@ def test_pack_zero_kv_tokens_become_neutral(dt):
     np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8))
     assert np.all(np.isneginf(wa[:, 1])) and np.all(wa[:, 0] == lse.numpy().reshape(B, N, Hpr).transpose(1, 0, 2)[:, 0])
 
+
+
+def test_fp8_worked_example():
+    """Two fp8 peers merged by the oracle, worked by hand.  Codes: peer 0 =
+    (0x38, 0x7E, 0x01, 0x7F) = (1, 448, 2^-9, NaN), peer 1 = (0x3C, 0xFE,
+    0x00, 0x40) = (1.5, -448, 0, 2).  Equal LSEs weigh each by 1/2: out =
+    (1.25, 0, 2^-10, 1) (the NaN partial counts as 0).  LSEs (0, ln 3) weigh
+    them 1/4 and 3/4: out = (1.375, -224, 2^-11, 1.5), and G = ln 4."""
+    o = np.array([[0x38, 0x7E, 0x01, 0x7F], [0x3C, 0xFE, 0x00, 0x40]], np.uint8).reshape(2, 1, 1, 4)
+    out, g, _, _ = orc.combine(o, np.zeros((2, 1, 1), np.float32), "fp8", False)
+    np.testing.assert_array_equal(out.reshape(-1), [1.25, 0.0, 2.0 ** -10, 1.0])
+    assert abs(g.item() - math.log(2.0)) < 1e-15
+    # ln 3 rounded to fp32 moves the weights off 1/4 and 3/4 by about 1e-8
+    lse = np.array([0.0, math.log(3.0)], np.float32).reshape(2, 1, 1)
+    out, g, _, _ = orc.combine(o, lse, "fp8", False)
+    np.testing.assert_allclose(out.reshape(-1), [1.375, -224.0, 2.0 ** -11, 1.5], rtol=1e-7, atol=0)
+    assert abs(g.item() - math.log(4.0)) < 1e-7
