@@ -96,3 +96,21 @@ def test_inplace_beyond_one_launch():
     check_lse(g[ts].cpu().numpy(), gr)
     del part, lse, out, g
     torch.cuda.empty_cache()
+
+
+def test_combine_beyond_one_launch_fp8():
+    """The same split with an fp8 payload (D = 16: 16-byte rows), random
+    codes including the two NaN codes (guarded to 0)."""
+    N, Hpr, D, B = 2, H_ROWS, 16, TOKENS
+    say("combine beyond one launch, fp8", B, Hpr, D)
+    g8 = torch.Generator(device=DEV).manual_seed(10)
+    codes = torch.randint(0, 256, (N, B, Hpr, D), generator=g8, device=DEV, dtype=torch.uint8)
+    rl = randn((N, B, Hpr), 11, torch.float32, 3.0)
+    out, g = ops.dcp_lse_combine(codes.view(torch.float8_e4m3fn), rl, is_lse_base_on_e=False)
+    torch.cuda.synchronize()
+    bs = sample(B, 12)
+    ref, gr, mag, _ = orc.combine(codes[:, bs].cpu().numpy(), rl[:, bs].cpu().numpy(), "fp8", True)
+    check_out(decode(out.view(torch.uint8)[bs].cpu().numpy(), "fp8"), ref, mag, "fp8")
+    check_lse(g[bs].cpu().numpy(), gr)
+    del codes, rl, out, g
+    torch.cuda.empty_cache()
