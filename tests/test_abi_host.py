@@ -218,3 +218,15 @@ def test_header_compiles_as_c_and_the_c_client_links(tmp_path):
     exe = __graft_entry__.build_c_client(str(tmp_path / "client"))
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+def test_binding_constants_match_the_header():
+    """The dtype, LSE-base and status codes the Python binding passes are the
+    values include/dcpmerge.h gives them."""
+    text = open(HEADER).read()
+    values = {name: int(v) for name, v in re.findall(r"\b(DCP_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+    for name in ("DCP_F32", "DCP_F16", "DCP_BF16", "DCP_FP8_E4M3", "DCP_LSE_BASE_E", "DCP_LSE_BASE_2"):
+        assert values[name] == getattr(_lib, name), name
+    for code, name in _lib.STATUS.items():
+        assert values[name] == code, name
+    assert sorted(v for k, v in values.items() if k.startswith("DCP_ERR_") or k == "DCP_OK") == sorted(_lib.STATUS)
