@@ -103,7 +103,7 @@ def algorithmic_bytes(key, B=None):
 class A2AWorkload:
     """Interleaved or split pack + combine, `layers` distinct buffer sets."""
 
-    def __init__(self, key, B, layers, dev):
+    def __init__(self, key, B, layers, dev, kv=False):
         import numpy as np
         import torch
 
@@ -126,6 +126,13 @@ class A2AWorkload:
         else:
             o0 = torch.from_numpy(o).to(dev)
         l0 = torch.from_numpy(self.inp["lse"]).to(dev)
+        # with kv: the pack reads each rank's KV length per token and sends the
+        # neutral pair itself where it is 0 (interleaved workloads only)
+        self.kv = None
+        if kv:
+            if w.layout != "interleaved" or self.inp["kv_len"] is None:
+                raise SystemExit("--kv-len needs a workload with per-rank KV lengths (dsv3, longctx, dsv3fp8)")
+            self.kv = torch.from_numpy(self.inp["kv_len"].astype(np.int32)).to(dev)
         self.src, self.lse, self.stk, self.out, self.glse = [], [], [], [], []
         cls = sim.StackedSplit if w.layout == "split" else sim.StackedInterleaved
         # distinct buffer sets: one per layer while that stays under 16 GiB, else
@@ -154,7 +161,7 @@ class A2AWorkload:
 
     def pack(self, l):
         k = l % self.distinct
-        self.stk[k].pack(self.src[k], self.lse[k])
+        self.stk[k].pack(self.src[k], self.lse[k], kv_len=self.kv)
 
     def combine(self, l):
         k = l % self.distinct
@@ -162,7 +169,7 @@ class A2AWorkload:
 
     def pack_rank0(self, l):
         k = l % self.distinct
-        self.stk[k].pack_rank(0, self.src[k][0], self.lse[k][0])
+        self.stk[k].pack_rank(0, self.src[k][0], self.lse[k][0], kv_len=None if self.kv is None else self.kv[0])
 
     def combine_dest0(self, l):
         k = l % self.distinct
@@ -213,7 +220,7 @@ class A2AWorkload:
                                 w.N, w.B, w.H, w.Hpr, w.D, w.dtype, "2" if w.base2 else "e", w.layout,
                                 self.layers),
                 "N": w.N, "B": w.B, "H": w.H, "D": w.D, "payload_dtype": w.dtype, "layers": self.layers,
-                "layout": w.layout,
+                "layout": w.layout, "kv_len_in_pack": self.kv is not None,
                 "distinct_buffer_sets": self.distinct}
 
     def cpu_sample(self, budget_s):
@@ -232,7 +239,8 @@ class A2AWorkload:
             send = np.empty((w.N, w.N, w.B, w.Hpr, w.D + lpd), npdt)
             pay, words = orc.interleaved_views_np(send, w.D, w.dtype)
             for r in range(w.N):
-                orc.pack(inp["out"][r], inp["lse"][r], pay[r], words[r], w.N)
+                kv = None if self.kv is None else np.ascontiguousarray(inp["kv_len"][r], np.int32)
+                orc.pack(inp["out"][r], inp["lse"][r], pay[r], words[r], w.N, kv_len=kv)
             for p in range(w.N):
                 orc.combine(pay[:, p], words[:, p], w.dtype, w.base2)
             t_total += time.perf_counter() - t0
@@ -595,6 +603,8 @@ def main():
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--layers", type=int, default=61)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--kv-len", action="store_true",
+                    help="the pack reads per-rank KV lengths and neutralises tokens whose length is 0")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--summarize-counters", default=None)
     args = ap.parse_args()
@@ -618,7 +628,7 @@ def main():
     elif args.workload == "kimi-rs":
         wl = ReduceScatterWorkload(args.B, dev)
     else:
-        wl = A2AWorkload(args.workload, args.B, args.layers, dev)
+        wl = A2AWorkload(args.workload, args.B, args.layers, dev, kv=args.kv_len)
 
     if args.counter_run:
         counter_run(wl)

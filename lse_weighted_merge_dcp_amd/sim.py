@@ -37,9 +37,10 @@ class StackedInterleaved:
         packs its own send buffer (one launch)."""
         ops.dcp_pack_a2a_send(out, lse, self.payload, self.words, kv_len=kv_len)
 
-    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor) -> None:
-        """Rank r's own pack at its real shape: out [B,H,D], lse [B,H]."""
-        ops.dcp_pack_a2a_send(out, lse, self.payload[r], self.words[r])
+    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+        """Rank r's own pack at its real shape: out [B,H,D], lse [B,H] (kv_len
+        [B] int32 optional)."""
+        ops.dcp_pack_a2a_send(out, lse, self.payload[r], self.words[r], kv_len=kv_len)
 
     def recv(self):
         """Received buffers of all destinations: [dst, src, B, Hpr, D] and [dst, src, B, Hpr]."""
