@@ -73,9 +73,11 @@ class StackedSplit:
         ops.dcp_pack_a2a_send(out, lse, self.partial_o.permute(0, 3, 1, 2, 4),
                               self.stats[..., 0].permute(0, 3, 1, 2), kv_len=kv_len)
 
-    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor) -> None:
-        """Rank r's own pack at its real shape: out [B,H,D], lse [B,H]."""
-        ops.dcp_pack_a2a_send(out, lse, self.partial_o[r].permute(2, 0, 1, 3), self.stats[r][..., 0].permute(2, 0, 1))
+    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+        """Rank r's own pack at its real shape: out [B,H,D], lse [B,H] (kv_len
+        [B] int32 optional)."""
+        ops.dcp_pack_a2a_send(out, lse, self.partial_o[r].permute(2, 0, 1, 3), self.stats[r][..., 0].permute(2, 0, 1),
+                              kv_len=kv_len)
 
     def exchange(self) -> None:
         """Stand-in for the all-to-all: o_out[dst, b, hl, src] = partial_o[src, b, hl, dst]."""
