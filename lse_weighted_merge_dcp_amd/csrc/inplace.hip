@@ -311,9 +311,16 @@ hipError_t run_n(const InplaceArgs& a, hipStream_t stream) {
 template <typename DT>
 hipError_t run_dt(const InplaceArgs& a, int V, hipStream_t stream) {
     if (V == 16) {
-        const int64_t chunks = a.D * DT::esize / 16;
-        if (chunks >= 48) return run_n<DT, 16, 64>(a, stream);
-        return run_n<DT, 16, 16>(a, stream);
+        if constexpr (DT::esize == 1) {
+            // fp8 in 8-byte vectors (8 fp32 values per rank and lane): the
+            // 16-byte form spills registers with all 16 ranks stacked
+            if (a.D / 8 >= 48) return run_n<DT, 8, 64>(a, stream);
+            return run_n<DT, 8, 16>(a, stream);
+        } else {
+            const int64_t chunks = a.D * DT::esize / 16;
+            if (chunks >= 48) return run_n<DT, 16, 64>(a, stream);
+            return run_n<DT, 16, 16>(a, stream);
+        }
     }
     if (a.P == 1) return run<DT, DT::esize, 64, 0, 1, 2>(a, stream);
     return run<DT, DT::esize, 64, 0>(a, stream);

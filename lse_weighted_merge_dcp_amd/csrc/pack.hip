@@ -59,9 +59,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
     // payload so they never delay it.
     const char* lsrc = nullptr;
     char* ldst = nullptr;
+    // each row's KV length (when given) is read after all payload loads have
+    // gone out, so that no payload load waits for it
+    const char* kvp[U];
+    int lrow = -1;   // which of the U rows the lane's LSE word belongs to
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         pl[u] = false;
+        kvp[u] = nullptr;
         const uint32_t vrow = (blk * (uint32_t)U + (uint32_t)u) * (4u * RPW) + wave * RPW + g;
         if (vrow < k.vrows) {
             const uint32_t row = (k.steps == 1) ? vrow : fdiv(vrow, k.f_steps);
@@ -73,20 +78,32 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
             const uint32_t p = fdiv(h, k.f_Hpr);
             const uint32_t hl = h - p * k.Hpr;
             const uint32_t c = step * LPR + li;
-            const bool neutral = k.kv != nullptr && load_word(k.kv + r * k.kv_R + b * k.kv_B) == 0u;
+            if (k.kv != nullptr) kvp[u] = k.kv + r * k.kv_R + b * k.kv_B;
             if (k.dst != nullptr && c < k.chunks) {
-                v[u] = neutral ? vzero<V>() : vload<V>(k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V);
+                v[u] = vload<V>(k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V);
                 dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + hl * k.d_H + (int64_t)c * V;
                 pl[u] = true;
             }
             if (k.dst_lse != nullptr && step == 0 && li == (uint32_t)u) {
-                lsrc = neutral ? nullptr : k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H;
+                lsrc = k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H;
+                lrow = u;
                 ldst = k.dst_lse + r * k.dl_R + p * k.dl_N + b * k.dl_B + hl * k.dl_H;
             }
         }
     }
-    uint32_t lw = kNegInfBits;   // the neutral pair's LSE
+    uint32_t lw = 0u;
     if (lsrc != nullptr) lw = load_word(lsrc);
+    // a token this rank owns no KV for is sent as the neutral pair (zeros and
+    // a -inf LSE); its rows were read and are dropped here
+    if (k.kv != nullptr) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (kvp[u] != nullptr && load_word(kvp[u]) == 0u) {
+                v[u] = vzero<V>();
+                if (lrow == u) lw = kNegInfBits;
+            }
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
         if (pl[u]) vstore<V>(dp[u], v[u]);
