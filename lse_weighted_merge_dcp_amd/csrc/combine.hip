@@ -247,8 +247,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 // HOIST issues the payload loads right after the LSE load, so the LSE
 // reduction runs while the payload is in flight: one memory round trip per
 // wave instead of two.  That wins when the launch is latency-bound (few
-// rows, every wave resident at once); on large launches loading after the
-// weights measured faster, and the launcher picks by size.  Small launches
+// rows, every wave resident at once) and again on the largest launches;
+// in between (thousands of rows, such as one decode layer's combine)
+// loading after the weights measured faster, and the launcher picks by
+// size.  Small launches
 // also use one-wave workgroups (WPB = 1): the rows then spread over up to
 // four times as many CUs, and each CU's load pipeline serves fewer of them.
 template <typename DT, int NT, bool HOIST, int WPB, bool NTS>
@@ -343,6 +345,12 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
 // crossover on MI355X between the latency-bound and the bandwidth-bound
 // regime of the row-per-wave kernel).
 constexpr int64_t kHoistMaxRows = 2048;
+// ... and so do launches of at least this many, in 4-wave workgroups
+// (measured on MI355X: the long-context B = 256 combine, 32768 tasks, 96.9 ->
+// 95.8 us; the Kimi-K3-shaped reduce-scatter merge 5.05 -> 4.98 ms; the
+// DeepSeek-V3-shaped combine, 8192 tasks, 11.9 -> 13.3 us in HOIST order,
+// hence the gap).
+constexpr int64_t kHoistMinRowsLarge = 32768;
 
 template <typename DT, int V, int LPR, int NT>
 hipError_t run(const CombineArgs& a, hipStream_t stream) {
@@ -388,6 +396,11 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
                 if (rows <= kHoistMaxRows)
                     e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false>, dim3((uint32_t)rows), dim3(64), stream,
                                       k);
+                else if (rows >= kHoistMinRowsLarge)
+                    e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 4, true>, dim3((uint32_t)blocks),
+                                               dim3(256), stream, k)
+                               : launch_kernel(combine_wave_kernel<DT, NT, true, 4, false>, dim3((uint32_t)blocks),
+                                               dim3(256), stream, k);
                 else if (nt_out)
                     e = launch_kernel(combine_wave_kernel<DT, NT, false, 4, true>, dim3((uint32_t)blocks), dim3(256),
                                       stream, k);
