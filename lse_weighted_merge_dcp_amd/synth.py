@@ -212,20 +212,40 @@ def kimi_lse(w: Workload) -> np.ndarray:
     return lse
 
 
+# tokens per seeded draw of the in-place workload's device partials
+KIMI_TOKEN_BLOCK = 2048
+
+
+def _kimi_block_generator(w: Workload, rank: int, t0: int, device) -> torch.Generator:
+    s = np.random.SeedSequence([w.seed, w.index, rank, 4, t0]).generate_state(1, np.uint64)[0]
+    return torch.Generator(device=device).manual_seed(int(s & 0x7FFFFFFFFFFFFFFF))
+
+
 def kimi_partial_device(w: Workload, device, dtype=torch.float32) -> torch.Tensor:
     """The in-place workload's partial stack [N,T,H,D] drawn directly in device
     memory (24 GiB at the full size): N(0,1) from a device generator seeded per
-    (rank, token block).  Deterministic for a given seed on a given device type."""
+    (rank, block of KIMI_TOKEN_BLOCK tokens).  Deterministic for a given seed
+    on a given device type."""
     N, T, H, D = w.N, w.B, w.H, w.D
     part = torch.empty((N, T, H, D), dtype=dtype, device=device)
-    block = 2048
     for r in range(N):
-        for t0 in range(0, T, block):
-            t1 = min(T, t0 + block)
-            s = np.random.SeedSequence([w.seed, w.index, r, 4, t0]).generate_state(1, np.uint64)[0]
-            g = torch.Generator(device=device).manual_seed(int(s & 0x7FFFFFFFFFFFFFFF))
-            part[r, t0:t1].normal_(0.0, 1.0, generator=g)
+        for t0 in range(0, T, KIMI_TOKEN_BLOCK):
+            t1 = min(T, t0 + KIMI_TOKEN_BLOCK)
+            part[r, t0:t1].normal_(0.0, 1.0, generator=_kimi_block_generator(w, r, t0, device))
     return part
+
+
+def kimi_partial_block_device(w: Workload, device, t0: int, dtype=torch.float32) -> torch.Tensor:
+    """Tokens [t0, t0 + KIMI_TOKEN_BLOCK) of kimi_partial_device's stack,
+    [N, tokens, H, D], drawn again from the same seeds (t0 must start a
+    block): the pristine partials of that block, for checking a merge that
+    overwrote them."""
+    assert t0 % KIMI_TOKEN_BLOCK == 0 and 0 <= t0 < w.B
+    t1 = min(w.B, t0 + KIMI_TOKEN_BLOCK)
+    blk = torch.empty((w.N, t1 - t0, w.H, w.D), dtype=dtype, device=device)
+    for r in range(w.N):
+        blk[r].normal_(0.0, 1.0, generator=_kimi_block_generator(w, r, t0, device))
+    return blk
 
 
 def dcp_local_len(L: np.ndarray, n: int, rank: int) -> np.ndarray:

@@ -188,6 +188,37 @@ def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
     check_lse(gg.cpu().numpy(), gr)
 
 
+@pytest.mark.parametrize("dt,N,D,B", [
+    ("bf16", 8, 512, 4096),     # 32768 rows, 32 MiB of output: payload loads first, plain stores
+    ("bf16", 8, 512, 8192),     # 65536 rows, 64 MiB: payload loads first, nontemporal stores
+    ("f32", 2, 1000, 1100),     # 35200 row segments (4 per row), 34 MiB
+    ("fp8", 4, 1024, 8192),     # 65536 rows of 1 KB fp8, 64 MiB
+])
+def test_row_per_wave_kernel_guards_large_launches(dt, N, D, B):
+    """Launches of 32768 row segments and more issue the payload loads before
+    the LSE reduction, and merged outputs of 64 MiB and more go out with
+    nontemporal stores: NaN and +-inf planted in the payload force the
+    guarded re-read there too, with special LSE values and all-neutral rows;
+    every output element and every G is compared."""
+    say("row-per-wave large launch", dt, N, D, B)
+    Hpr = 8
+    g = torch.Generator().manual_seed(N * 7 + D + B)
+    o = synth.to_storage(torch.randn(N, B, Hpr, D, generator=g), dt)
+    rng = np.random.default_rng(N + D + B)
+    lse = rng.normal(0, 4, size=(N, B, Hpr)).astype(np.float32)
+    for k in range(300):
+        lse[rng.integers(N), rng.integers(B), rng.integers(Hpr)] = [np.nan, np.inf, -np.inf][k % 3]
+    lse[:, 0, 0] = -np.inf
+    lse[:, B - 1, Hpr - 1] = -np.inf
+    special_o = synth.to_storage(torch.tensor([math.nan, math.inf, -math.inf]), dt)
+    for k in range(600):
+        o[rng.integers(N), rng.integers(B), rng.integers(Hpr), rng.integers(D)] = special_o[k % 3]
+    out, gg = ops.dcp_lse_combine(to_dev(o, dt, DEV), torch.from_numpy(lse).to(DEV), is_lse_base_on_e=False)
+    ref, gr, mag, _ = orc.combine(o, lse, dt, True)
+    check_out(decode(to_host(out, dt), dt), ref, mag, dt)
+    check_lse(gg.cpu().numpy(), gr)
+
+
 @pytest.mark.parametrize("dt,N,B,Hpr,D", [
     ("bf16", 8, 5, 4, 512),      # row-per-wave kernel, latency order
     ("bf16", 8, 160, 16, 512),   # row-per-wave kernel, bandwidth order (2560 rows)

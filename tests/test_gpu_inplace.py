@@ -1,6 +1,6 @@
 """GPU parity of dcp_lse_combine_inplace against the fp64 oracle, including
 the full-size in-place workload (8 ranks x [16384, 96, 512] fp32 = 24 GiB)
-checked on sampled rows."""
+and its reduce-scatter flavour, both checked on every row."""
 import numpy as np
 import pytest
 import torch
@@ -139,44 +139,52 @@ def test_reduce_scatter_flavour_through_strided_combine():
     check_lse(g.cpu().numpy(), gr)
 
 
-def test_inplace_full_size_sampled():
-    """8 x [16384, 96, 512] fp32 partials (24 GiB) merged in one call, in the
-    launch configurations the benchmark times: first the reduce-scatter
-    flavour (every rank's head slice, in one launch; the partials must stay
-    untouched), then in place; 3000 sampled (t, h) rows are checked (scaled
-    partials of all ranks, merged row, G) for both."""
+# ---------------------------------------------------------------------------
+# Full size, every row: 8 x [16384, 96, 512] fp32 partials (24 GiB) merged in
+# the launch configurations the benchmark times -- first the reduce-scatter
+# flavour (every rank's head slice in one launch; the partials stay as they
+# are), then in place.  Each test below takes one block of 2048 tokens: it
+# draws that block's pristine partials again from their seeds, runs the
+# oracle on them in pieces of 256 tokens, and compares every scaled partial
+# of all 8 ranks, every merged row and every G of both calls.
+# ---------------------------------------------------------------------------
+FULL_PIECE = 256
+
+
+@pytest.fixture(scope="module")
+def full_kimi():
     w = synth.WORKLOADS["kimi"]
     say("inplace full size", w.describe())
     part = synth.kimi_partial_device(w, DEV)
     lse_np = synth.kimi_lse(w)
     lse = torch.from_numpy(lse_np).to(DEV)
-    rng = np.random.default_rng(99)
-    T, H = w.B, w.H
-    ts = rng.integers(0, T, size=3000)
-    hs = rng.integers(0, H, size=3000)
-    # make sure sampled rows include special LSE entries
-    sp = np.argwhere(~np.isfinite(lse_np))[:200]
-    ts = np.concatenate([ts, sp[:, 1]]); hs = np.concatenate([hs, sp[:, 2]])
-    ti, hi = torch.from_numpy(ts).to(DEV), torch.from_numpy(hs).to(DEV)
-    before = part[:, ti, hi].cpu().numpy()             # [N, S, D] inputs of the sampled rows
-    # reduce-scatter flavour first (it leaves the partials untouched)
     rs_out, rs_g = sim.reduce_scatter_merge(part, lse)
     torch.cuda.synchronize()
-    rs_got_out = rs_out[ti, hi].cpu().numpy()
-    rs_got_g = rs_g[ti, hi].cpu().numpy()
-    assert np.array_equal(part[:, ti, hi].cpu().numpy().view(np.uint32), before.view(np.uint32))
-    del rs_out, rs_g
+    # the reduce-scatter flavour writes no partial: every byte is still the
+    # seeded draw (this also proves the block-wise redraw below exact)
+    for t0 in range(0, w.B, synth.KIMI_TOKEN_BLOCK):
+        blk = synth.kimi_partial_block_device(w, DEV, t0)
+        assert torch.equal(part[:, t0:t0 + blk.shape[1]].view(torch.int32), blk.view(torch.int32)), t0
+        del blk
     out, g = ops.cp_lse_combine_inplace(part, lse, return_lse=True)
     torch.cuda.synchronize()
-    after = part[:, ti, hi].cpu().numpy()
-    got_out = out[ti, hi].cpu().numpy()
-    got_g = g[ti, hi].cpu().numpy()
-    S = len(ts)
-    scaled, ref, gr, mag = orc.inplace(before.reshape(w.N, S, 1, w.D), lse_np[:, ts, hs].reshape(w.N, S, 1), "f32", False)
-    check_scaled(after, scaled.reshape(w.N, S, w.D), "f32")
-    check_out(got_out, ref.reshape(S, w.D), mag.reshape(S, w.D), "f32")
-    check_lse(got_g, gr.reshape(S))
-    check_out(rs_got_out, ref.reshape(S, w.D), mag.reshape(S, w.D), "f32")
-    check_lse(rs_got_g, gr.reshape(S))
-    del part, out
+    say("inplace full size: both calls done")
+    yield w, part, lse_np, out, g, rs_out, rs_g
+    del part, out, g, rs_out, rs_g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("t0", list(range(0, synth.WORKLOADS["kimi"].B, synth.KIMI_TOKEN_BLOCK)))
+def test_inplace_full_size_every_row(full_kimi, t0):
+    w, part, lse_np, out, g, rs_out, rs_g = full_kimi
+    say("inplace full size: tokens", t0, t0 + synth.KIMI_TOKEN_BLOCK)
+    pristine = synth.kimi_partial_block_device(w, DEV, t0).cpu().numpy()
+    for p0 in range(0, pristine.shape[1], FULL_PIECE):
+        a, b = t0 + p0, t0 + p0 + FULL_PIECE
+        scaled, ref, gr, mag = orc.inplace(pristine[:, p0:p0 + FULL_PIECE], lse_np[:, a:b], "f32", False)
+        where = "tokens [%d, %d)" % (a, b)
+        check_scaled(part[:, a:b], scaled, "f32", "scaled partials, " + where)
+        check_out(out[a:b], ref, mag, "f32", "in-place merge, " + where)
+        check_lse(g[a:b].cpu().numpy(), gr)
+        check_out(rs_out[a:b], ref, mag, "f32", "reduce-scatter merge, " + where)
+        check_lse(rs_g[a:b].cpu().numpy(), gr)
