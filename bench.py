@@ -159,13 +159,14 @@ class A2AWorkload:
         self.bytes_pack, self.bytes_combine = nb["pack"], nb["combine"]
         self.bytes_layer = self.bytes_pack + self.bytes_combine
 
-    def pack(self, l):
+    def pack(self, l, timing=None):
         k = l % self.distinct
-        self.stk[k].pack(self.src[k], self.lse[k], kv_len=self.kv)
+        self.stk[k].pack(self.src[k], self.lse[k], kv_len=self.kv, timing=timing)
 
-    def combine(self, l):
+    def combine(self, l, timing=None):
         k = l % self.distinct
-        self.stk[k].combine(is_lse_base_on_e=not self.w.base2, out=self.out[k], out_lse=self.glse[k])
+        self.stk[k].combine(is_lse_base_on_e=not self.w.base2, out=self.out[k], out_lse=self.glse[k],
+                            timing=timing)
 
     def pack_rank0(self, l):
         k = l % self.distinct
@@ -198,8 +199,8 @@ class A2AWorkload:
         """The step's calls in order, each with the kernel it launches."""
         fns = []
         for l in range(self.layers):
-            fns.append(("pack", lambda l=l: self.pack(l)))
-            fns.append(("combine", lambda l=l: self.combine(l)))
+            fns.append(("pack", lambda l=l, **kw: self.pack(l, **kw)))
+            fns.append(("combine", lambda l=l, **kw: self.combine(l, **kw)))
         return fns
 
     def kernels(self):
@@ -277,10 +278,11 @@ class InplaceWorkload:
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
         self.bytes_call = algorithmic_bytes("kimi", B)["inplace"]
 
-    def run(self):
+    def run(self, timing=None):
         from lse_weighted_merge_dcp_amd import ops
 
-        ops.cp_lse_combine_inplace(self.part, self.lse, out=self.out, out_lse=self.glse, return_lse=True)
+        ops.cp_lse_combine_inplace(self.part, self.lse, out=self.out, out_lse=self.glse, return_lse=True,
+                                   timing=timing)
 
     def restore(self):
         self.part.copy_(self.pristine)
@@ -361,10 +363,10 @@ class ReduceScatterWorkload:
         print("# generated %s in %.1f s" % (w.describe(), time.time() - t0), file=sys.stderr, flush=True)
         self.bytes_call = algorithmic_bytes("kimi-rs", B)["combine"]
 
-    def run(self):
+    def run(self, timing=None):
         from lse_weighted_merge_dcp_amd import sim
 
-        sim.reduce_scatter_merge(self.part, self.lse, out=self.out, out_lse=self.glse)
+        sim.reduce_scatter_merge(self.part, self.lse, out=self.out, out_lse=self.glse, timing=timing)
 
     def kernels(self):
         return [("combine", self.bytes_call, [self.run])]
@@ -547,14 +549,15 @@ def in_step_us(named, reps, restore=None):
     may then fall behind the device, which leaves gaps between kernels but
     not inside the timed ones.)
     The launches of one kernel per replay carry timing events on their own
-    dispatches (ops.time_next_call), so no marker packet sits between the
-    kernels; the replays take the kernels in turn.  `named` is the step as
+    dispatches (the timing= argument: the same kernels through the
+    measurement library), so no marker packet sits between the kernels; the
+    replays take the kernels in turn.  `named` is the step as
     (kernel name, call) pairs.  Returns ({name: us per launch}, {name:
     median device span in ms of the replays that timed it, from its first
     timed start to its last timed end})."""
     import torch
 
-    from lse_weighted_merge_dcp_amd import ops, timing
+    from lse_weighted_merge_dcp_amd import timing
 
     order = []
     for n, _ in named:
@@ -583,8 +586,9 @@ def in_step_us(named, reps, restore=None):
         timed = [i for i, (n, _) in enumerate(named) if n == name]
         for i, (n, f) in enumerate(named):
             if n == name:
-                ops.time_next_call(*events[i])
-            f()
+                f(timing=events[i])
+            else:
+                f()
         torch.cuda.synchronize()
         for i in timed:
             total[name] += events[i][0].elapsed_us(events[i][1])

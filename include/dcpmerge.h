@@ -16,12 +16,13 @@
  *     allocates, frees, zero-fills, synchronises or copies to the host, so the
  *     calls can be captured in a HIP graph.
  *   - Work is enqueued only on `stream` (a hipStream_t passed as void*; NULL is
- *     the null stream).  Calls keep no state between them, apart from the
- *     one-call timing request of dcp_time_next_call.
+ *     the null stream).  Calls keep no state between them, so calls on
+ *     different streams may run concurrently.
  *   - Payload tensors hold `dtype` elements; the innermost (D) dimension is
  *     contiguous.  Every other stride is given in ELEMENTS of that tensor's
  *     own type: payload strides in payload elements, LSE strides in fp32
- *     words.  Strides must be >= 0.
+ *     words.  Strides must be >= 0 and at most 2^56, and each view must span
+ *     less than 2^60 bytes; otherwise DCP_ERR_STRIDE.
  *   - Payload pointers must be aligned to the element size and LSE pointers
  *     to 4 bytes.  Faster kernels are chosen when the payload rows are
  *     4-byte aligned and D * element size is a multiple of 16 bytes.
@@ -32,10 +33,12 @@
  *   - Errors are detected on the host before anything is enqueued: on any
  *     error nothing is written.  A zero-sized call (R, B or T = 0) is DCP_OK.
  *   - Size limits: the heads of one token (H, or Hpr for the combine) times
- *     (D * element size / 32 + 1) must not exceed 2^25, H <= 2^24 and
- *     D * element size <= 2^28 bytes; otherwise DCP_ERR_SHAPE.  R, B and T
- *     are limited only by memory: the library splits them over several
- *     launches.
+ *     (D * element size / 32 + 1) must not exceed 2^25, H <= 2^24,
+ *     D * element size <= 2^28 bytes, and one call moves at most 2^56
+ *     payload bytes; otherwise DCP_ERR_SHAPE.  Within that, R, B and T are
+ *     limited only by memory: the library splits them over several
+ *     launches.  (These limits keep every size and offset the library
+ *     computes inside int64; no device holds memory near them.)
  *   - Leading dimension R ("R independent problems") is an extension for
  *     running several ranks' calls in one launch, e.g. all N simulated ranks
  *     stacked in one GPU's memory.  R = 1 is the single call the pages
@@ -75,11 +78,10 @@ enum {
     DCP_ERR_HEADS_NOT_DIVISIBLE = -3, /* dcp_pack: H % N != 0                               */
     DCP_ERR_DTYPE = -4,               /* dtype is not a dcp_dtype                           */
     DCP_ERR_LSE_BASE = -5,            /* lse_base is not a dcp_lse_base                     */
-    DCP_ERR_STRIDE = -6,              /* a stride is negative                               */
+    DCP_ERR_STRIDE = -6,              /* a stride negative or too large, a view too long    */
     DCP_ERR_ALIGN = -7,               /* payload not element-aligned, LSE not 4-byte aligned */
     DCP_ERR_HEAD_RANGE = -8,          /* in-place: not 0 <= h0 < h1 <= H                    */
-    DCP_ERR_LAUNCH = -9,              /* the HIP kernel launch failed                       */
-    DCP_ERR_CAPTURE = -10             /* timing events requested on a capturing stream      */
+    DCP_ERR_LAUNCH = -9               /* the HIP kernel launch failed                       */
 };
 
 /* Number of payload elements one fp32 LSE occupies when it is interleaved at
@@ -114,15 +116,18 @@ const char* dcp_status_str(int status);
  *
  * kv_len (nullable) holds the rank-local KV length of every (r, b) as int32.
  * Where it is 0 the rank owns no KV for that token, and the pack sends the
- * neutral pair instead of the partial: payload 0 and LSE -inf for all H heads,
- * without reading src (the fixup_zero_kv_rows pass of sglang PR #33926 report,
- * 实现拆解 item 3, fused into the pack).  Non-zero lengths change nothing.
+ * neutral pair instead of the partial: payload 0 and LSE -inf for all H heads
+ * (the fixup_zero_kv_rows pass of sglang PR #33926 report, 实现拆解 item 3,
+ * fused into the pack).  Non-zero lengths change nothing.  src_o and src_lse
+ * are still read for every (r, b, h), zero-KV tokens included (the length is
+ * read while the rows are in flight, and their bytes are then dropped), so
+ * they must be readable device memory for every token.
  *
  * Strides: src_o (so_R, so_B, so_H) elements; src_lse (sl_R, sl_B, sl_H)
  * words; dst_o (do_R, do_N, do_B, do_H) elements; dst_lse (dl_R, dl_N, dl_B,
  * dl_H) words; kv_len (kl_R, kl_B) int32 elements.  Errors: DCP_ERR_NULL,
  * _SHAPE (R, B < 0; N, H, D < 1), _HEADS_NOT_DIVISIBLE, _DTYPE, _STRIDE,
- * _ALIGN (also kv_len not 4-byte aligned), _CAPTURE, _LAUNCH.
+ * _ALIGN (also kv_len not 4-byte aligned), _LAUNCH.
  */
 int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
              const float* src_lse, int64_t sl_R, int64_t sl_B, int64_t sl_H,
@@ -156,8 +161,7 @@ int dcp_pack(const void* src_o, int64_t so_R, int64_t so_B, int64_t so_H,
  * the same out and out_lse, with the partials left untouched;
  * strides (ro_R, ro_N, ro_B, ro_H) elements; recv_lse (rl_R, rl_N, rl_B, rl_H)
  * words; out (oo_R, oo_B, oo_H) elements; out_lse (ol_R, ol_B, ol_H) words.
- * Errors: DCP_ERR_NULL, _SHAPE, _DTYPE, _LSE_BASE, _STRIDE, _ALIGN, _CAPTURE,
- * _LAUNCH.
+ * Errors: DCP_ERR_NULL, _SHAPE, _DTYPE, _LSE_BASE, _STRIDE, _ALIGN, _LAUNCH.
  */
 int dcp_unpack_combine(const void* recv_o, int64_t ro_R, int64_t ro_N, int64_t ro_B, int64_t ro_H,
                        const float* recv_lse, int64_t rl_R, int64_t rl_N, int64_t rl_B, int64_t rl_H,
@@ -186,7 +190,7 @@ int dcp_unpack_combine(const void* recv_o, int64_t ro_R, int64_t ro_N, int64_t r
  * Strides: partial (p_N, p_T, p_H) elements for (j, t, h); lse (l_N, l_T,
  * l_H) words; out (o_T, o_H) elements; out_lse (ol_T, ol_H) words.
  * Errors: DCP_ERR_NULL, _SHAPE (also P < 1 or rank0 + P > N), _DTYPE,
- * _LSE_BASE, _STRIDE, _ALIGN, _HEAD_RANGE, _CAPTURE, _LAUNCH.
+ * _LSE_BASE, _STRIDE, _ALIGN, _HEAD_RANGE, _LAUNCH.
  */
 int dcp_lse_combine_inplace(void* partial, int64_t p_N, int64_t p_T, int64_t p_H,
                             const float* lse, int64_t l_N, int64_t l_T, int64_t l_H,
@@ -196,28 +200,6 @@ int dcp_lse_combine_inplace(void* partial, int64_t p_N, int64_t p_T, int64_t p_H
                             int64_t N, int64_t P, int64_t rank0,
                             int64_t T, int64_t H, int64_t D,
                             int dtype, int lse_base, void* stream);
-
-/* Kernel timing for the next compute call made on the calling thread.
- *
- * Not an operation of the merge itself: a measurement hook, for callers that
- * want the device time of one call inside a longer stream of work.  Markers
- * recorded between kernels (hipEventRecord) add a packet, and usually a cache
- * release, to the stream, which stretches the very kernels they time; here
- * the events travel with the call's own kernel dispatches instead.
- *
- * The next dcp_pack, dcp_unpack_combine or dcp_lse_combine_inplace issued by
- * this thread records `start_event` (a hipEvent_t, or NULL) when its first
- * kernel starts and `stop_event` (or NULL) when its last kernel ends.  The
- * request applies to that one call and is then cleared, whatever the call
- * returns; a call that launches nothing (zero-sized, rejected) leaves both
- * events as they were.  Calling this again before that replaces the request;
- * NULL, NULL cancels it.  The caller owns the events; they belong to the
- * device the call runs on and are read with hipEventElapsedTime.  Create
- * them with hipEventDisableSystemFence so that the runtime adds no
- * system-scope cache release to the timed kernels.  A timed call made on a stream that is being
- * captured returns DCP_ERR_CAPTURE (nothing enqueued), because a capture does
- * not keep the events.  Returns DCP_OK. */
-int dcp_time_next_call(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -8,8 +8,7 @@ merge -- with a thin ctypes binding.  The shared library is loaded on first
 use and every call fails loudly if it is missing.
 """
 from ._lib import DcpError, DcpLaunchError
-from .ops import (cp_lse_combine_inplace, dcp_lse_combine, dcp_pack_a2a_send, interleaved_views,
-                  lse_pack_dim, time_next_call)
+from .ops import cp_lse_combine_inplace, dcp_lse_combine, dcp_pack_a2a_send, interleaved_views, lse_pack_dim
 
 __all__ = ["DcpError", "DcpLaunchError", "cp_lse_combine_inplace", "dcp_lse_combine", "dcp_pack_a2a_send",
-           "interleaved_views", "lse_pack_dim", "time_next_call"]
+           "interleaved_views", "lse_pack_dim"]

@@ -24,7 +24,6 @@ STATUS = {
     -7: "DCP_ERR_ALIGN",
     -8: "DCP_ERR_HEAD_RANGE",
     -9: "DCP_ERR_LAUNCH",
-    -10: "DCP_ERR_CAPTURE",
 }
 
 _I64 = ctypes.c_int64
@@ -47,7 +46,6 @@ SIGNATURES = {
                             _VP, _I64, _I64, _I64,
                             _I64, _I64, _I64, _I64, _I64,
                             _INT, _INT, _VP], _INT),
-    "dcp_time_next_call": ([_VP, _VP], _INT),
     "dcp_lse_combine_inplace": ([_VP, _I64, _I64, _I64,
                                  _VP, _I64, _I64, _I64,
                                  _I64, _I64,

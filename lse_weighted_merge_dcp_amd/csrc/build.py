@@ -1,9 +1,16 @@
-"""Build libdcpmerge.so for gfx950 with hipcc (cross-compiles without a GPU).
+"""Build libdcpmerge.so (and its measurement twin libdcpmerge_bench.so) for
+gfx950 with hipcc (cross-compiles without a GPU).
 
     python -m lse_weighted_merge_dcp_amd.csrc.build
 
-Objects go to csrc/_build/; the shared library lands next to the Python
-binding (lse_weighted_merge_dcp_amd/libdcpmerge.so), where the binding loads it.
+Objects go to csrc/_build/; the shared libraries land next to the Python
+binding (lse_weighted_merge_dcp_amd/), where the binding loads them.
+
+libdcpmerge.so exports exactly the calls of include/dcpmerge.h.
+libdcpmerge_bench.so links the same kernel objects behind the dcpb_* calls of
+csrc/dcpmerge_bench.h (timing events on the kernels' own dispatches) and
+exports nothing else; only measurement code loads it.  A linker version
+script fixes each library's exported names.
 """
 from __future__ import annotations
 
@@ -16,8 +23,18 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["api.cpp", "pack.hip", "combine.hip", "inplace.hip"]
+SOURCES = ["api.cpp", "pack.hip", "combine.hip", "inplace.hip", "bench_api.cpp"]
 LIB = os.path.join(PKG, "libdcpmerge.so")
+BENCH_LIB = os.path.join(PKG, "libdcpmerge_bench.so")
+# exported names of each library (everything else is local)
+EXPORTS = {
+    LIB: ["dcp_lse_pack_dim", "dcp_status_str", "dcp_pack", "dcp_unpack_combine", "dcp_lse_combine_inplace"],
+    BENCH_LIB: ["dcpb_pack", "dcpb_unpack_combine", "dcpb_lse_combine_inplace"],
+}
+OBJECTS = {
+    LIB: ["api", "pack", "combine", "inplace"],
+    BENCH_LIB: ["bench_api", "api", "pack", "combine", "inplace"],
+}
 ARCH = "gfx950"
 
 # Packed fp32 instructions are switched off for every HIP source; the host
@@ -46,19 +63,30 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print("\n".join(noise), file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libdcpmerge.so (always rebuilds)."""
-    bdir = os.path.join(HERE, "_build")
-    os.makedirs(bdir, exist_ok=True)
-    objs = [os.path.join(bdir, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+def _link(lib: str, bdir: str, verbose: bool) -> None:
+    script = os.path.join(bdir, os.path.basename(lib) + ".map")
+    with open(script, "w") as f:
+        f.write("{\n  global:\n%s  local: *;\n};\n" % "".join("    %s;\n" % n for n in EXPORTS[lib]))
+    objs = [os.path.join(bdir, o + ".o") for o in OBJECTS[lib]]
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,--version-script=" + script,
+           "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libdcpmerge.so and
+    libdcpmerge_bench.so (always rebuilds).  Returns libdcpmerge.so's path."""
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    objs = [os.path.join(bdir, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(5, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
+    for lib in (LIB, BENCH_LIB):
+        _link(lib, bdir, verbose)
     return LIB
 
 

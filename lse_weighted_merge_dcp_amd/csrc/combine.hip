@@ -395,20 +395,20 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             if constexpr (V == 16 && LPR == 64 && NT > 0) {
                 if (rows <= kHoistMaxRows)
                     e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false>, dim3((uint32_t)rows), dim3(64), stream,
-                                      k);
+                                      k, a.timing);
                 else if (rows >= kHoistMinRowsLarge)
                     e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 4, true>, dim3((uint32_t)blocks),
-                                               dim3(256), stream, k)
+                                               dim3(256), stream, k, a.timing)
                                : launch_kernel(combine_wave_kernel<DT, NT, true, 4, false>, dim3((uint32_t)blocks),
-                                               dim3(256), stream, k);
+                                               dim3(256), stream, k, a.timing);
                 else if (nt_out)
                     e = launch_kernel(combine_wave_kernel<DT, NT, false, 4, true>, dim3((uint32_t)blocks), dim3(256),
-                                      stream, k);
+                                      stream, k, a.timing);
                 else
                     e = launch_kernel(combine_wave_kernel<DT, NT, false, 4, false>, dim3((uint32_t)blocks), dim3(256),
-                                      stream, k);
+                                      stream, k, a.timing);
             } else {
-                e = launch_kernel(combine_kernel<DT, V, LPR, NT>, dim3((uint32_t)blocks), dim3(256), stream, k);
+                e = launch_kernel(combine_kernel<DT, V, LPR, NT>, dim3((uint32_t)blocks), dim3(256), stream, k, a.timing);
             }
             if (e != hipSuccess) return e;
         }

@@ -16,6 +16,13 @@ constexpr int dtype_esize(int dt) {
     return dt == DT_F32 ? 4 : dt == DT_F16 || dt == DT_BF16 ? 2 : dt == DT_FP8 ? 1 : 0;
 }
 
+// Timing events a call attaches to its own kernel dispatches (measurement
+// only; the library's exported calls never set them).
+struct CallTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // Pack (and the plain strided row copy the N == 1 shortcuts use):
 // for r < R, b < B, h < H with p = h / Hpr, hl = h % Hpr
 //   dst[r, p, b, hl, 0:row_bytes] = src[r, b, h, 0:row_bytes]
@@ -36,6 +43,7 @@ struct PackArgs {
     int64_t R, B, H, Hpr;
     int64_t row_bytes;
     int esize;
+    CallTiming* timing = nullptr;   // nullable: events for this call's dispatches
 };
 
 // Out-of-place combine over the peer axis N (see dcp_unpack_combine).
@@ -51,6 +59,7 @@ struct CombineArgs {
     int64_t R, N, B, Hpr, D;
     int dtype;
     bool base2;
+    CallTiming* timing = nullptr;   // nullable: events for this call's dispatches
 };
 
 // In-place merge (see dcp_lse_combine_inplace).
@@ -66,32 +75,24 @@ struct InplaceArgs {
     int64_t N, P, rank0, T, H, D, h0, h1;
     int dtype;
     bool base2;
+    CallTiming* timing = nullptr;   // nullable: events for this call's dispatches
 };
-
-// Timing events the running entry-point call attaches to its own kernel
-// dispatches (requested with dcp_time_next_call).  `start` goes on the
-// call's first launch only; `stop` on every launch, so that it ends up on
-// the last one.  Both null: plain launches.
-struct CallTiming {
-    hipEvent_t start = nullptr;
-    hipEvent_t stop = nullptr;
-};
-CallTiming& call_timing();  // the calling thread's, for the running call
 
 // Launch kernel(arg) and return that launch's own status.  (Reading the
 // thread's last error after a launch would also report, and clear, a stale
-// error the caller left from an unrelated call.)  With timing events set the
-// events travel with the dispatch itself, so no marker is added to the
-// stream between kernels.
+// error the caller left from an unrelated call.)  With timing events (t not
+// null) the events travel with the dispatch itself, so no marker is added to
+// the stream between kernels: `start` goes on the call's first launch only,
+// `stop` on every launch, so that it ends up on the last one.
 template <typename Arg>
-inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream, const Arg& arg) {
+inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream, const Arg& arg,
+                                CallTiming* t) {
     void* args[] = {const_cast<Arg*>(&arg)};
-    CallTiming& t = call_timing();
-    if (t.start == nullptr && t.stop == nullptr)
+    if (t == nullptr || (t->start == nullptr && t->stop == nullptr))
         return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
-    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream, t.start,
-                                      t.stop, 0);
-    t.start = nullptr;
+    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream, t->start,
+                                      t->stop, 0);
+    t->start = nullptr;
     return e;
 }
 

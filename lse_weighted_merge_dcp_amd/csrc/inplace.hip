@@ -279,7 +279,7 @@ hipError_t run(const InplaceArgs& a, hipStream_t stream) {
         k.f_steps = make_fastdiv(k.steps);
         k.base2 = a.base2 ? 1 : 0;
         const int64_t blocks = (rows + RPB - 1) / RPB;
-        const hipError_t e = launch_kernel(inplace_kernel<DT, V, LPR, NT, PB, U, NTS>, dim3((uint32_t)blocks), dim3(256), stream, k);
+        const hipError_t e = launch_kernel(inplace_kernel<DT, V, LPR, NT, PB, U, NTS>, dim3((uint32_t)blocks), dim3(256), stream, k, a.timing);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

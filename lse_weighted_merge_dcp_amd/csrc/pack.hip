@@ -248,15 +248,15 @@ bool stream_layout(const PackArgs& a) {
 }
 
 template <bool TWO>
-hipError_t launch_stream(const StreamK& k, bool nt_source, hipStream_t stream) {
+hipError_t launch_stream(const StreamK& k, bool nt_source, hipStream_t stream, CallTiming* t) {
     if (k.nsteps >= kStreamWide) {
         const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
         if (nt_source)
-            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO>, dim3(blocks), dim3(512), stream, k);
-        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO>, dim3(blocks), dim3(512), stream, k);
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO>, dim3(blocks), dim3(512), stream, k, t);
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO>, dim3(blocks), dim3(512), stream, k, t);
     }
     const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO>, dim3(blocks), dim3(256), stream, k);
+    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO>, dim3(blocks), dim3(256), stream, k, t);
 }
 
 hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
@@ -297,8 +297,8 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.f_N = make_fastdiv(k.N);
             k.f_B = make_fastdiv(k.B);
             k.f_Wd = make_fastdiv(k.Wd);
-            const hipError_t e = k.Wd < 256 ? launch_stream<true>(k, nt_source, stream)
-                                             : launch_stream<false>(k, nt_source, stream);
+            const hipError_t e = k.Wd < 256 ? launch_stream<true>(k, nt_source, stream, a.timing)
+                                             : launch_stream<false>(k, nt_source, stream, a.timing);
             if (e != hipSuccess) return e;
         }
     }
@@ -347,7 +347,7 @@ hipError_t run_u(const PackArgs& a, hipStream_t stream) {
             k.f_B = make_fastdiv(k.B);
             k.f_Hpr = make_fastdiv(k.Hpr);
             const int64_t blocks = (vrows + RPB - 1) / RPB;
-            const hipError_t e = launch_kernel(pack_kernel<V, LPR, U>, dim3((uint32_t)blocks), dim3(256), stream, k);
+            const hipError_t e = launch_kernel(pack_kernel<V, LPR, U>, dim3((uint32_t)blocks), dim3(256), stream, k, a.timing);
             if (e != hipSuccess) return e;
         }
     }

@@ -13,11 +13,15 @@ torch.empty) and streams.  There is no CPU or PyTorch fallback.
       sglang PR #34213 report, code excerpt of cp_lse_ag_out_rs_mha
   lse_pack_dim(dtype), interleaved_views(send, D)
       vLLM PR #41160 report, 实现拆解 item 2; sglang PR #34651 report, 实现拆解 item 2
-  time_next_call(start, stop)
-      a measurement hook, not a step of the method: device time of one call
 
 Every entry point also accepts a leading R dimension (R independent calls
 in one launch, e.g. all simulated ranks stacked in one GPU's memory).
+
+The three compute calls take an optional `timing=(start, stop)` pair of
+timing.Event for measurement: that one call then runs the same kernels
+through the separate measurement library (timing.py), with the events on
+the kernels' own dispatches.  Without it (the default) the call goes to
+libdcpmerge.so, which keeps no state.
 """
 from __future__ import annotations
 
@@ -37,6 +41,18 @@ def _dt(t: torch.Tensor) -> int:
 
 def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _invoke(name: str, args: tuple, timing) -> None:
+    """Call `name` of libdcpmerge.so with the marshalled arguments, or its
+    timed twin of the measurement library when timing events are given."""
+    if timing is None:
+        st = getattr(_lib.lib(), name)(*args)
+    else:
+        from . import timing as _timing
+
+        st = _timing.call_timed(name, args, *timing)
+    _lib.check(st, name)
 
 
 def _require(cond: bool, msg: str) -> None:
@@ -91,7 +107,7 @@ def interleaved_views(send: torch.Tensor, D: int) -> Tuple[torch.Tensor, torch.T
 
 
 def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor, dst_lse: torch.Tensor,
-                      kv_len: Optional[torch.Tensor] = None) -> None:
+                      kv_len: Optional[torch.Tensor] = None, timing=None) -> None:
     """Scatter out [B,H,D] / lse [B,H] into dst_o [N,B,H/N,D] / dst_lse
     [N,B,H/N] (any strides): head h goes to peer h // (H/N) as local head
     h % (H/N).  With a leading R dimension on all four, R packs run at once.
@@ -122,19 +138,18 @@ def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor,
         _require(kv_len.dtype == torch.int32 and tuple(kv_len.shape) == (R, B), "kv_len must be int32 [R,B] / [B]")
         kl = kv_len.stride()
     so, sl, do, dl = out.stride(), lse.stride(), dst_o.stride(), dst_lse.stride()
-    st = _lib.lib().dcp_pack(
+    _invoke("dcp_pack", (
         out.data_ptr(), so[0], so[1], so[2],
         lse.data_ptr(), sl[0], sl[1], sl[2],
         dst_o.data_ptr(), do[0], do[1], do[2], do[3],
         dst_lse.data_ptr(), dl[0], dl[1], dl[2], dl[3],
         kv_len.data_ptr() if kv_len is not None else None, kl[0], kl[1],
-        R, N, B, H, D, _dt(out), _stream(out))
-    _lib.check(st, "dcp_pack")
+        R, N, B, H, D, _dt(out), _stream(out)), timing)
 
 
 def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on_e: bool = True,
                     return_lse: bool = True, out: Optional[torch.Tensor] = None,
-                    out_lse: Optional[torch.Tensor] = None):
+                    out_lse: Optional[torch.Tensor] = None, timing=None):
     """LSE-weighted merge over axis 0 of recv_o [N,B,Hpr,D] (any strides) and
     recv_lse [N,B,Hpr].  Returns (out [B,Hpr,D], global LSE [B,Hpr] or None).
     The global LSE is in the input's base.  With a leading R dimension
@@ -162,14 +177,13 @@ def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on
         _lse_ok(out_lse, "out_lse")
     ro, rl, oo = recv_o.stride(), recv_lse.stride(), out.stride()
     ol = out_lse.stride() if out_lse is not None else (0, 0, 0)
-    st = _lib.lib().dcp_unpack_combine(
+    _invoke("dcp_unpack_combine", (
         recv_o.data_ptr(), ro[0], ro[1], ro[2], ro[3],
         recv_lse.data_ptr(), rl[0], rl[1], rl[2], rl[3],
         out.data_ptr(), oo[0], oo[1], oo[2],
         out_lse.data_ptr() if out_lse is not None else None, ol[0], ol[1], ol[2],
         R, N, B, Hpr, D, _dt(recv_o),
-        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(recv_o))
-    _lib.check(st, "dcp_unpack_combine")
+        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(recv_o)), timing)
     if not batched:
         out = out[0]
         out_lse = out_lse[0] if out_lse is not None else None
@@ -179,7 +193,7 @@ def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on
 def cp_lse_combine_inplace(partial: torch.Tensor, lse: torch.Tensor, h0: int = 0, h1: Optional[int] = None,
                            rank0: int = 0, is_lse_base_on_e: bool = True, return_lse: bool = False,
                            out: Optional[torch.Tensor] = None, out_lse: Optional[torch.Tensor] = None,
-                           want_out: bool = True):
+                           want_out: bool = True, timing=None):
     """In-place merge: partial [P,T,H,D] holds ranks rank0..rank0+P-1 of the
     N = lse.shape[0] ranks; lse [N,T,H].  Every held partial is overwritten
     with nan_to_num(o) * w, and out [T,h1-h0,D] = sum of the held scaled
@@ -206,24 +220,12 @@ def cp_lse_combine_inplace(partial: torch.Tensor, lse: torch.Tensor, h0: int = 0
     ps, ls = partial.stride(), lse.stride()
     os_ = out.stride() if out is not None else (0, 0, 0)
     ols = out_lse.stride() if out_lse is not None else (0, 0)
-    st = _lib.lib().dcp_lse_combine_inplace(
+    _invoke("dcp_lse_combine_inplace", (
         partial.data_ptr(), ps[0], ps[1], ps[2],
         lse.data_ptr(), ls[0], ls[1], ls[2],
         h0, h1,
         out.data_ptr() if out is not None else None, os_[0], os_[1],
         out_lse.data_ptr() if out_lse is not None else None, ols[0], ols[1],
         N, P, rank0, T, H, D, _dt(partial),
-        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(partial))
-    _lib.check(st, "dcp_lse_combine_inplace")
+        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(partial)), timing)
     return (out, out_lse) if return_lse else out
-
-
-def time_next_call(start=None, stop=None) -> None:
-    """Attach timing events to the kernels of the next libdcpmerge call made
-    on this thread: `start` (a timing.Event or None) records when its first
-    kernel starts, `stop` when its last kernel ends.  The request covers one
-    call of the C library; a wrapper above that raises before reaching the
-    library leaves it pending.  A timed call on a capturing stream raises
-    DcpError (DCP_ERR_CAPTURE)."""
-    h = [None if e is None else e.handle for e in (start, stop)]
-    _lib.check(_lib.lib().dcp_time_next_call(h[0], h[1]), "dcp_time_next_call")

@@ -32,29 +32,30 @@ class StackedInterleaved:
         self.send = torch.empty((N, N, B, H // N, D + self.lpd), dtype=dtype, device=device)
         self.payload, self.words = ops.interleaved_views(self.send, D)
 
-    def pack(self, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+    def pack(self, out: torch.Tensor, lse: torch.Tensor, kv_len=None, timing=None) -> None:
         """out [N,B,H,D], lse [N,B,H] (kv_len [N,B] int32 optional): every rank
         packs its own send buffer (one launch)."""
-        ops.dcp_pack_a2a_send(out, lse, self.payload, self.words, kv_len=kv_len)
+        ops.dcp_pack_a2a_send(out, lse, self.payload, self.words, kv_len=kv_len, timing=timing)
 
-    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor, kv_len=None, timing=None) -> None:
         """Rank r's own pack at its real shape: out [B,H,D], lse [B,H] (kv_len
         [B] int32 optional)."""
-        ops.dcp_pack_a2a_send(out, lse, self.payload[r], self.words[r], kv_len=kv_len)
+        ops.dcp_pack_a2a_send(out, lse, self.payload[r], self.words[r], kv_len=kv_len, timing=timing)
 
     def recv(self):
         """Received buffers of all destinations: [dst, src, B, Hpr, D] and [dst, src, B, Hpr]."""
         return self.payload.transpose(0, 1), self.words.transpose(0, 1)
 
-    def combine_dest(self, p: int, is_lse_base_on_e: bool, out=None, out_lse=None):
+    def combine_dest(self, p: int, is_lse_base_on_e: bool, out=None, out_lse=None, timing=None):
         """Destination p's own combine at its real shape (its received [N, B, Hpr, D])."""
         ro, rl = self.recv()
-        return ops.dcp_lse_combine(ro[p], rl[p], is_lse_base_on_e=is_lse_base_on_e, out=out, out_lse=out_lse)
+        return ops.dcp_lse_combine(ro[p], rl[p], is_lse_base_on_e=is_lse_base_on_e, out=out, out_lse=out_lse,
+                                   timing=timing)
 
-    def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None):
+    def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None, timing=None):
         ro, rl = self.recv()
         return ops.dcp_lse_combine(ro, rl, is_lse_base_on_e=is_lse_base_on_e, return_lse=return_lse,
-                                   out=out, out_lse=out_lse)
+                                   out=out, out_lse=out_lse, timing=timing)
 
 
 class StackedSplit:
@@ -69,15 +70,15 @@ class StackedSplit:
         self.o_out = torch.empty_like(self.partial_o)
         self.stats_out = torch.empty_like(self.stats)
 
-    def pack(self, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+    def pack(self, out: torch.Tensor, lse: torch.Tensor, kv_len=None, timing=None) -> None:
         ops.dcp_pack_a2a_send(out, lse, self.partial_o.permute(0, 3, 1, 2, 4),
-                              self.stats[..., 0].permute(0, 3, 1, 2), kv_len=kv_len)
+                              self.stats[..., 0].permute(0, 3, 1, 2), kv_len=kv_len, timing=timing)
 
-    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor, kv_len=None) -> None:
+    def pack_rank(self, r: int, out: torch.Tensor, lse: torch.Tensor, kv_len=None, timing=None) -> None:
         """Rank r's own pack at its real shape: out [B,H,D], lse [B,H] (kv_len
         [B] int32 optional)."""
         ops.dcp_pack_a2a_send(out, lse, self.partial_o[r].permute(2, 0, 1, 3), self.stats[r][..., 0].permute(2, 0, 1),
-                              kv_len=kv_len)
+                              kv_len=kv_len, timing=timing)
 
     def exchange(self) -> None:
         """Stand-in for the all-to-all: o_out[dst, b, hl, src] = partial_o[src, b, hl, dst]."""
@@ -88,18 +89,19 @@ class StackedSplit:
         """Strided receive views [dst, src, B, Hpr, D] and [dst, src, B, Hpr] (no copy)."""
         return self.o_out.permute(0, 3, 1, 2, 4), self.stats_out[..., 0].permute(0, 3, 1, 2)
 
-    def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None):
+    def combine(self, is_lse_base_on_e: bool, return_lse: bool = True, out=None, out_lse=None, timing=None):
         ro, rl = self.recv()
         return ops.dcp_lse_combine(ro, rl, is_lse_base_on_e=is_lse_base_on_e, return_lse=return_lse,
-                                   out=out, out_lse=out_lse)
+                                   out=out, out_lse=out_lse, timing=timing)
 
-    def combine_dest(self, p: int, is_lse_base_on_e: bool, out=None, out_lse=None):
+    def combine_dest(self, p: int, is_lse_base_on_e: bool, out=None, out_lse=None, timing=None):
         """Destination p's own combine at its real shape (its received [N, B, Hpr, D])."""
         ro, rl = self.recv()
-        return ops.dcp_lse_combine(ro[p], rl[p], is_lse_base_on_e=is_lse_base_on_e, out=out, out_lse=out_lse)
+        return ops.dcp_lse_combine(ro[p], rl[p], is_lse_base_on_e=is_lse_base_on_e, out=out, out_lse=out_lse,
+                                   timing=timing)
 
 
-def reduce_scatter_merge(partial: torch.Tensor, lse: torch.Tensor, out=None, out_lse=None):
+def reduce_scatter_merge(partial: torch.Tensor, lse: torch.Tensor, out=None, out_lse=None, timing=None):
     """Reduce-scatter flavour of the in-place merge for all N ranks at once.
 
     partial [N, T, H, D] and lse [N, T, H] hold every rank's partial result.
@@ -119,5 +121,5 @@ def reduce_scatter_merge(partial: torch.Tensor, lse: torch.Tensor, out=None, out
         out = torch.empty((T, H, D), dtype=partial.dtype, device=partial.device)
     if out_lse is None:
         out_lse = torch.empty((T, H), dtype=torch.float32, device=partial.device)
-    ops.dcp_lse_combine(partial, lse, is_lse_base_on_e=True, out=out, out_lse=out_lse)
+    ops.dcp_lse_combine(partial, lse, is_lse_base_on_e=True, out=out, out_lse=out_lse, timing=timing)
     return out, out_lse

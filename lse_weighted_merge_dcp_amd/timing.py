@@ -1,16 +1,64 @@
-"""HIP events for timing single libdcpmerge calls (dcp_time_next_call).
+"""Device time of single libdcpmerge calls, for measurement only.
+
+A timed call runs the same kernels through libdcpmerge_bench.so (built from
+the same sources, csrc/dcpmerge_bench.h), whose dcpb_* calls take two HIP
+events and attach them to the call's own kernel dispatches: the start event
+records when the first kernel starts, the stop event when the last one ends.
+libdcpmerge.so itself takes no events and keeps no state.  ops.py sends a
+call here when it is given `timing=(start, stop)`.
 
 The events come from the HIP runtime this process already runs (torch and
-libdcpmerge share it) and are created with hipEventDisableSystemFence, so
+the libraries share it) and are created with hipEventDisableSystemFence, so
 that attaching them to a kernel dispatch adds no system-scope cache release
-to the kernel being timed.  Measurement plumbing only: nothing here touches
-the merge's data.
+to the kernel being timed.  Nothing here touches the merge's data.
 """
 from __future__ import annotations
 
 import ctypes
+import os
 
 from . import _lib
+
+BENCH_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcpmerge_bench.so")
+DCPB_ERR_CAPTURE = -10
+_bench = None
+
+
+class CaptureError(_lib.DcpError):
+    """A timed call was made on a stream that is being captured (nothing
+    was enqueued): a capture does not keep dispatch events."""
+
+    def __init__(self, fn: str):
+        ValueError.__init__(self, "%s failed: DCPB_ERR_CAPTURE (timing events on a capturing stream)" % fn)
+        self.status = DCPB_ERR_CAPTURE
+
+
+def bench_lib():
+    """libdcpmerge_bench.so, loaded on first use (raises if it is not built)."""
+    global _bench
+    if _bench is None:
+        if not os.path.exists(BENCH_LIB_PATH):
+            raise ImportError("libdcpmerge_bench.so is not built (expected at %s); run "
+                              "`python -m lse_weighted_merge_dcp_amd.csrc.build`" % BENCH_LIB_PATH)
+        h = ctypes.CDLL(BENCH_LIB_PATH)
+        for name in ("dcp_pack", "dcp_unpack_combine", "dcp_lse_combine_inplace"):
+            args, res = _lib.SIGNATURES[name]
+            fn = getattr(h, "dcpb_" + name[len("dcp_"):])
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + list(args)
+            fn.restype = res
+        _bench = h
+    return _bench
+
+
+def call_timed(name: str, args: tuple, start: "Event | None", stop: "Event | None") -> int:
+    """Run libdcpmerge's `name` with the marshalled `args` through its timed
+    twin dcpb_*; returns the status of include/dcpmerge.h (raises
+    CaptureError for DCPB_ERR_CAPTURE)."""
+    fn = getattr(bench_lib(), "dcpb_" + name[len("dcp_"):])
+    st = fn(None if start is None else start.handle, None if stop is None else stop.handle, *args)
+    if st == DCPB_ERR_CAPTURE:
+        raise CaptureError(name)
+    return st
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
@@ -22,7 +70,7 @@ def hip_runtime():
     dependencies if nothing loaded it before)."""
     global _hip
     if _hip is None:
-        _lib.lib()
+        bench_lib()
         path = None
         with open("/proc/self/maps") as f:
             for line in f:

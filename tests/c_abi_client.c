@@ -14,9 +14,9 @@
  * the payload type; DIR/lse.bin the LSEs [N, B, H] fp32.  Written: DIR/send.bin
  * (the send buffers [N src, N peer, B, H/N, D + lpd]), DIR/comb.bin (the
  * merged rows [N dst, B, H/N, D]) and DIR/g.bin (the global LSE [N, B, H/N]).
- * The caller checks them against the oracle.  The combine is timed with
- * dcp_time_next_call (printed as "timed combine: ... us").  Exit status 0 on
- * success.
+ * The caller checks them against the oracle.  The combine is timed with two
+ * HIP events recorded around it on the stream (printed as "timed combine:
+ * ... us").  Exit status 0 on success.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -112,19 +112,18 @@ int main(int argc, char** argv) {
                   N, N, B, H, D, dtype, stream);
     if (st != DCP_OK) { fprintf(stderr, "dcp_pack: %s\n", dcp_status_str(st)); return 1; }
 
-    /* combine: destination p reads send[:, p] -- axes (dst, src) swapped;
-     * its kernels carry timing events on their own dispatches */
+    /* combine: destination p reads send[:, p] -- axes (dst, src) swapped */
     hipEvent_t ev0, ev1;
-    HIP_OK(hipEventCreateWithFlags(&ev0, hipEventDisableSystemFence));
-    HIP_OK(hipEventCreateWithFlags(&ev1, hipEventDisableSystemFence));
-    st = dcp_time_next_call(ev0, ev1);
-    if (st != DCP_OK) { fprintf(stderr, "dcp_time_next_call: %s\n", dcp_status_str(st)); return 1; }
+    HIP_OK(hipEventCreate(&ev0));
+    HIP_OK(hipEventCreate(&ev1));
+    HIP_OK(hipEventRecord(ev0, stream));
     st = dcp_unpack_combine(d_send, sN, sR, sB, sH,
                             d_words, sN * e / 4, sR * e / 4, sB * e / 4, sH * e / 4,
                             d_comb, B * Hpr * D, Hpr * D, D,
                             (float*)d_g, B * Hpr, Hpr, 1,
                             N, N, B, Hpr, D, dtype, base, stream);
     if (st != DCP_OK) { fprintf(stderr, "dcp_unpack_combine: %s\n", dcp_status_str(st)); return 1; }
+    HIP_OK(hipEventRecord(ev1, stream));
     HIP_OK(hipStreamSynchronize(stream));
     float ms = 0.0f;
     HIP_OK(hipEventElapsedTime(&ms, ev0, ev1));

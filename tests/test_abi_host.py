@@ -1,6 +1,8 @@
 """Host-side checks of the C ABI (no GPU, no kernel launch).
 
-* the shared library loads and exports every function include/dcpmerge.h declares;
+* the shared library loads and exports every function include/dcpmerge.h
+  declares, and nothing else; the measurement library libdcpmerge_bench.so
+  exports exactly the timed calls its own header declares;
 * dcp_lse_pack_dim and dcp_status_str;
 * every validation error is returned before anything is enqueued (the calls
   below use fake, never-dereferenced addresses; only rejected or zero-sized
@@ -30,27 +32,61 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dcp_\w+)\s*\(", text, re.M)))
 
 
+BENCH_HEADER = os.path.join(CSRC, "dcpmerge_bench.h")
+
+
+def declared_in(path, prefix):
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(%s\w+)\s*\(" % prefix, text, re.M)))
+
+
+def exported_functions(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True)
+    return sorted(set(re.findall(r" T (\w+)$", out.stdout, re.M)))
+
+
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["dcp_lse_combine_inplace", "dcp_lse_pack_dim", "dcp_pack",
-                                    "dcp_status_str", "dcp_time_next_call", "dcp_unpack_combine"]
+                                    "dcp_status_str", "dcp_unpack_combine"]
 
 
-def test_time_next_call_only_records_a_request():
-    """Arming and cancelling a timing request touches no device."""
+def test_library_exports_exactly_the_declared_symbols():
+    """libdcpmerge.so exports the calls of include/dcpmerge.h and nothing
+    else (no timing hook, no internal C++ symbol)."""
     lib = _lib.lib()
-    assert lib.dcp_time_next_call(None, None) == 0
-    assert lib.dcp_time_next_call(A, A + 256) == 0
-    assert lib.dcp_time_next_call(None, None) == 0
-
-
-def test_library_exports_every_declared_symbol():
-    lib = _lib.lib()
-    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True)
-    exported = set(re.findall(r" T (\w+)$", out.stdout, re.M))
+    assert exported_functions(_lib.LIB_PATH) == declared_functions()
     for name in declared_functions():
-        assert name in exported, name
         assert getattr(lib, name) is not None
         assert name in _lib.SIGNATURES
+
+
+def test_bench_library_exports_exactly_its_timed_calls():
+    """libdcpmerge_bench.so exports the dcpb_* calls of its header, one per
+    compute call of libdcpmerge, each with two event arguments in front."""
+    from lse_weighted_merge_dcp_amd import timing
+
+    declared = declared_in(BENCH_HEADER, "dcpb_")
+    assert declared == ["dcpb_lse_combine_inplace", "dcpb_pack", "dcpb_unpack_combine"]
+    assert exported_functions(timing.BENCH_LIB_PATH) == declared
+    lib = timing.bench_lib()
+    for name in declared:
+        assert len(getattr(lib, name).argtypes) == len(_lib.SIGNATURES["dcp_" + name[5:]][0]) + 2
+
+
+def test_bench_library_validates_like_the_library():
+    """A timed call with fake (never dereferenced) addresses is rejected with
+    the same status as the plain call, before any event or launch."""
+    from lse_weighted_merge_dcp_amd import timing
+
+    lib = timing.bench_lib()
+    args = list(dict(src_o=A, so_R=0, so_B=512, so_H=64, src_lse=A, sl_R=0, sl_B=8, sl_H=1,
+                     dst_o=A, do_R=0, do_N=256, do_B=128, do_H=64, dst_lse=A, dl_R=0, dl_N=4, dl_B=2, dl_H=1,
+                     kv_len=None, kl_R=0, kl_B=1, R=1, N=3, B=4, H=8, D=64, dtype=0, stream=None).values())
+    assert lib.dcpb_pack(A, A + 256, *args) == HEADS          # N = 3 does not divide H = 8
+    assert _lib.lib().dcp_pack(*args) == HEADS
+    args[-6], args[-5] = 2, 0                                  # N = 2, B = 0: a valid no-op
+    assert lib.dcpb_pack(A, A + 256, *args) == OK
+    assert _lib.lib().dcp_pack(*args) == OK
 
 
 def test_lse_pack_dim_and_status_strings():
@@ -109,6 +145,12 @@ def inplace(**kw):
     (dict(H=1 << 25, N=1), SHAPE), (dict(D=1 << 27), SHAPE),
     (dict(H=1 << 22, N=1), SHAPE), (dict(H=1 << 11, N=1, D=1 << 20), SHAPE),   # one token's rows > 2^25
     (dict(B=0), OK), (dict(R=0), OK), (dict(B=0, src_o=None), OK),
+    # limits that keep host arithmetic inside int64
+    (dict(so_B=(1 << 56) + 1), STRIDE), (dict(dl_H=(1 << 63) - 1), STRIDE), (dict(kl_R=1 << 60), STRIDE),
+    (dict(so_B=1 << 55, B=1 << 10), STRIDE), (dict(do_R=1 << 50, dl_R=1, R=1 << 12), STRIDE),
+    (dict(D=(1 << 63) - 1), SHAPE), (dict(D=(1 << 62) + 1, dtype=2), SHAPE),
+    (dict(R=1 << 40, B=1 << 40), SHAPE), (dict(B=(1 << 63) - 1, so_B=0, sl_B=0, do_B=0, dl_B=0), SHAPE),
+    (dict(so_B=1 << 56, B=1 << 20, dtype=3), STRIDE),
 ])
 def test_pack_validation(kw, code):
     assert pack(**kw) == code
@@ -122,6 +164,8 @@ def test_pack_validation(kw, code):
     (dict(recv_o=None), NULL), (dict(out=None), NULL), (dict(recv_lse=None), NULL),
     (dict(recv_lse=A + 1), ALIGN), (dict(out_lse=A + 2), ALIGN), (dict(out=A + 1, dtype=2), ALIGN),
     (dict(B=0), OK), (dict(R=0, out=None), OK),
+    (dict(ro_N=(1 << 56) + 1), STRIDE), (dict(ro_B=1 << 56, B=1 << 5), STRIDE), (dict(D=(1 << 62) + 3), SHAPE),
+    (dict(R=1 << 62, ro_R=0, rl_R=0, oo_R=0, ol_R=0), SHAPE),
 ])
 def test_combine_validation(kw, code):
     assert combine(**kw) == code
@@ -136,6 +180,9 @@ def test_combine_validation(kw, code):
     (dict(partial=None), NULL), (dict(lse=None), NULL),
     (dict(partial=A + 2), ALIGN), (dict(lse=A + 3), ALIGN), (dict(out=A + 2), ALIGN),
     (dict(T=0), OK),
+    (dict(rank0=(1 << 63) - 1), SHAPE), (dict(P=(1 << 63) - 1), SHAPE), (dict(N=1 << 62, P=1 << 61), SHAPE),
+    (dict(o_T=(1 << 56) + 1), STRIDE), (dict(p_N=1 << 58), STRIDE), (dict(T=1 << 30, p_T=1 << 40), STRIDE),
+    (dict(T=1 << 62, p_T=0, l_T=0, o_T=0, ol_T=0), SHAPE), (dict(D=(1 << 63) - 1), SHAPE),
 ])
 def test_inplace_validation(kw, code):
     assert inplace(**kw) == code

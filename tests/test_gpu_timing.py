@@ -1,7 +1,8 @@
-"""dcp_time_next_call: timing events travel with the next call's kernel
-dispatches, change nothing in its results, cover exactly one call, are
-cleared by a call that launches nothing or is rejected, and are refused
-while the stream is being captured."""
+"""Timed calls (libdcpmerge_bench.so, reached through ops' timing=(start,
+stop)): the events travel with the call's own kernel dispatches, change
+nothing in its results, are left unrecorded by a call that launches nothing
+or is rejected, and are refused while the stream is being captured.  Calls
+without events go to libdcpmerge.so, which takes no events at all."""
 import numpy as np
 import pytest
 import torch
@@ -34,18 +35,13 @@ def test_timed_calls_match_untimed():
     results = []
     for timed in (False, True):
         ev = [timing.Event() for _ in range(6)]
+        tm = [(ev[i], ev[i + 1]) if timed else None for i in (0, 2, 4)]
         send, pay, words = send_buffers()
-        if timed:
-            ops.time_next_call(ev[0], ev[1])
-        ops.dcp_pack_a2a_send(o, l, pay, words)
-        if timed:
-            ops.time_next_call(ev[2], ev[3])
-        comb, g = ops.dcp_lse_combine(pay, words, is_lse_base_on_e=True, return_lse=True)
+        ops.dcp_pack_a2a_send(o, l, pay, words, timing=tm[0])
+        comb, g = ops.dcp_lse_combine(pay, words, is_lse_base_on_e=True, return_lse=True, timing=tm[1])
         part = torch.stack([o.float() * (r + 1) for r in range(N)])
         lses = torch.stack([l - r for r in range(N)])
-        if timed:
-            ops.time_next_call(ev[4], ev[5])
-        merged, gl = ops.cp_lse_combine_inplace(part, lses, return_lse=True)
+        merged, gl = ops.cp_lse_combine_inplace(part, lses, return_lse=True, timing=tm[2])
         torch.cuda.synchronize()
         results.append([t.clone() for t in (send, comb, g, part, merged, gl)])
         if timed:
@@ -62,8 +58,7 @@ def test_timed_combine_matches_the_oracle():
     send, pay, words = send_buffers()
     ops.dcp_pack_a2a_send(o, l, pay, words)
     s, e = timing.Event(), timing.Event()
-    ops.time_next_call(s, e)
-    comb, g = ops.dcp_lse_combine(pay, words, is_lse_base_on_e=True, return_lse=True)
+    comb, g = ops.dcp_lse_combine(pay, words, is_lse_base_on_e=True, return_lse=True, timing=(s, e))
     torch.cuda.synchronize()
     assert s.elapsed_us(e) > 0
     host = send.cpu().view(torch.int16).numpy().view(np.uint16)
@@ -73,43 +68,37 @@ def test_timed_combine_matches_the_oracle():
     check_lse(g.cpu().numpy(), gr)
 
 
-def test_request_covers_one_call():
-    say("one call")
+def test_start_or_stop_alone():
+    say("one event")
     _, _, o, l = inputs()
     send, pay, words = send_buffers()
-    s, e = timing.Event(), timing.Event()
-    ops.time_next_call(s, e)
-    ops.dcp_pack_a2a_send(o, l, pay, words)
+    a, b = timing.Event(), timing.Event()
+    ops.dcp_pack_a2a_send(o, l, pay, words, timing=(a, None))
+    ops.dcp_pack_a2a_send(o, l, pay, words, timing=(None, b))
     torch.cuda.synchronize()
-    first = s.elapsed_us(e)
-    for _ in range(3):
-        ops.dcp_pack_a2a_send(o, l, pay, words)
-    torch.cuda.synchronize()
-    assert s.elapsed_us(e) == first
+    assert a.elapsed_us(b) > 0
 
 
-def test_call_without_launch_clears_request():
+def test_call_without_launch_records_nothing():
     say("zero-sized call")
     _, _, o, l = inputs()
     send, pay, words = send_buffers()
     s, e = timing.Event(), timing.Event()
-    ops.time_next_call(s, e)
-    ops.dcp_pack_a2a_send(o[:0], l[:0], pay[:, :0], words[:, :0])
+    ops.dcp_pack_a2a_send(o[:0], l[:0], pay[:, :0], words[:, :0], timing=(s, e))
     ops.dcp_pack_a2a_send(o, l, pay, words)
     torch.cuda.synchronize()
     with pytest.raises(RuntimeError):     # never recorded
         s.elapsed_us(e)
 
 
-def test_rejected_call_clears_request():
+def test_rejected_call_records_nothing():
     say("rejected call")
     _, _, o, l = inputs()
     send, pay, words = send_buffers()
     s, e = timing.Event(), timing.Event()
-    ops.time_next_call(s, e)
-    st = _lib.lib().dcp_pack(o.data_ptr(), 0, 0, 0, l.data_ptr(), 0, 0, 0,
-                             pay.data_ptr(), 0, 0, 0, 0, words.data_ptr(), 0, 0, 0, 0,
-                             None, 0, 0, 1, N, B, H, D, 7, None)
+    st = timing.bench_lib().dcpb_pack(s.handle, e.handle, o.data_ptr(), 0, 0, 0, l.data_ptr(), 0, 0, 0,
+                                      pay.data_ptr(), 0, 0, 0, 0, words.data_ptr(), 0, 0, 0, 0,
+                                      None, 0, 0, 1, N, B, H, D, 7, None)
     assert _lib.STATUS[st] == "DCP_ERR_DTYPE"
     ops.dcp_pack_a2a_send(o, l, pay, words)
     torch.cuda.synchronize()
@@ -128,9 +117,8 @@ def test_timed_call_refused_during_capture():
     s, e = timing.Event(), timing.Event()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        ops.time_next_call(s, e)
-        with pytest.raises(_lib.DcpError, match="DCP_ERR_CAPTURE"):
-            ops.dcp_pack_a2a_send(o, l, pay, words)
+        with pytest.raises(timing.CaptureError, match="DCPB_ERR_CAPTURE"):
+            ops.dcp_pack_a2a_send(o, l, pay, words, timing=(s, e))
         ops.dcp_pack_a2a_send(o, l, pay, words)     # untimed: captured as usual
     torch.cuda.synchronize()
     for _ in range(2):
