@@ -80,8 +80,14 @@ def _load(lib=None):
     if lib is not None:
         return lib
     if _lib is None:
-        build()
-        _lib = load_library(_LIB_PATH)
+        # DCP_ORACLE_LIB names another build of dcp_oracle.c to use instead
+        # (the tests run the pins against a sanitizer build this way)
+        other = os.environ.get("DCP_ORACLE_LIB")
+        if other:
+            _lib = load_library(other)
+        else:
+            build()
+            _lib = load_library(_LIB_PATH)
     return _lib
 
 
