@@ -168,21 +168,22 @@ class A2AWorkload:
         self.stk[k].combine(is_lse_base_on_e=not self.w.base2, out=self.out[k], out_lse=self.glse[k],
                             timing=timing)
 
-    def pack_rank0(self, l):
+    def pack_rank0(self, l, timing=None):
         k = l % self.distinct
-        self.stk[k].pack_rank(0, self.src[k][0], self.lse[k][0], kv_len=None if self.kv is None else self.kv[0])
+        self.stk[k].pack_rank(0, self.src[k][0], self.lse[k][0], kv_len=None if self.kv is None else self.kv[0],
+                              timing=timing)
 
-    def combine_dest0(self, l):
+    def combine_dest0(self, l, timing=None):
         k = l % self.distinct
-        self.stk[k].combine_dest(0, not self.w.base2, out=self.out[k][0], out_lse=self.glse[k][0])
+        self.stk[k].combine_dest(0, not self.w.base2, out=self.out[k][0], out_lse=self.glse[k][0], timing=timing)
 
     def per_rank(self):
         """One rank's pack and one destination's combine at their real shapes
         (1/N of the all-rank launches), over the same distinct layer buffers."""
         N = self.w.N
-        return [("pack", self.bytes_pack // N, [lambda l=l: self.pack_rank0(l) for l in range(self.layers)]),
+        return [("pack", self.bytes_pack // N, [lambda l=l, **kw: self.pack_rank0(l, **kw) for l in range(self.layers)]),
                 ("combine", self.bytes_combine // N,
-                 [lambda l=l: self.combine_dest0(l) for l in range(self.layers)])]
+                 [lambda l=l, **kw: self.combine_dest0(l, **kw) for l in range(self.layers)])]
 
     def hot_launches(self):
         """The step with one layer's buffers reused by every layer (cache-resident)."""
@@ -205,8 +206,9 @@ class A2AWorkload:
 
     def kernels(self):
         """(name, per-launch algorithmic bytes, list of launch closures)."""
-        return [("pack", self.bytes_pack, [lambda l=l: self.pack(l) for l in range(self.layers)]),
-                ("combine", self.bytes_combine, [lambda l=l: self.combine(l) for l in range(self.layers)])]
+        return [("pack", self.bytes_pack, [lambda l=l, **kw: self.pack(l, **kw) for l in range(self.layers)]),
+                ("combine", self.bytes_combine,
+                 [lambda l=l, **kw: self.combine(l, **kw) for l in range(self.layers)])]
 
     def step_bytes(self):
         return self.layers * self.bytes_layer
@@ -299,8 +301,8 @@ class InplaceWorkload:
 
         nbytes = algorithmic_bytes("kimi", self.w.B)["inplace_rank"]
 
-        def call():
-            ops.cp_lse_combine_inplace(self.part[0:1], self.lse, rank0=0, want_out=False)
+        def call(timing=None):
+            ops.cp_lse_combine_inplace(self.part[0:1], self.lse, rank0=0, want_out=False, timing=timing)
 
         return [("inplace", nbytes, [call])]
 
@@ -388,8 +390,8 @@ class ReduceScatterWorkload:
         g = torch.empty((self.w.B, hs), dtype=torch.float32, device=self.dev)
         torch.cuda.synchronize()
 
-        def call():
-            ops.dcp_lse_combine(recv, recv_lse, is_lse_base_on_e=True, out=out, out_lse=g)
+        def call(timing=None):
+            ops.dcp_lse_combine(recv, recv_lse, is_lse_base_on_e=True, out=out, out_lse=g, timing=timing)
 
         return [("combine", nbytes, [call])]
 
@@ -597,24 +599,272 @@ def in_step_us(named, reps, restore=None):
     return {n: total[n] / count[n] for n in order}, {n: round(percentiles(v)["p50"], 4) for n, v in spans.items()}
 
 
+# The headline workload (the largest decode configuration: long-context
+# decode, N = 16, B = 512) and the workloads reported beside it by default.
+HEADLINE = ("longctx", None)
+DEFAULT_SECONDARY = ("dsv3", "kimi")
+
+
+def make_workload(key, B, layers, dev, kv=False):
+    if key == "kimi":
+        return InplaceWorkload(B, dev)
+    if key == "kimi-rs":
+        return ReduceScatterWorkload(B, dev)
+    return A2AWorkload(key, B, layers, dev, kv=kv)
+
+
+def time_step(wl, steps, warmup):
+    """Capture the workload's step in one HIP graph, replay it `warmup`
+    times, then time exactly `steps` replays bracketed by synchronisations
+    (HIP events between replays give the per-step spread).  Returns (wall
+    seconds of the timed region, [ms of each step])."""
+    import torch
+
+    restore = getattr(wl, "restore", None)
+    step = [f for _, f in wl.named_step()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(warmup, 1)):
+            if restore:
+                restore()
+            for f in step:
+                f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in step:
+            f()
+    for _ in range(warmup):
+        if restore:
+            restore()
+        graph.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    if restore is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[2 * i].record()
+            graph.replay()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        # the in-place call destroys its input: restore it (untimed) before each step
+        wall = 0.0
+        for i in range(steps):
+            restore()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev[2 * i].record()
+            graph.replay()
+            ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+    del graph
+    return wall, [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+
+
+def launch_shape_of(fn):
+    """Launch shape of one call (launches, workgroups and threads of its
+    last launch), from the measurement library."""
+    import torch
+
+    from lse_weighted_merge_dcp_amd import timing
+
+    shape = timing.LaunchShape()
+    fn(timing=(None, None, shape))
+    torch.cuda.synchronize()
+    return shape
+
+
+def empty_floor_us(shape, count, reps):
+    """Per-launch time of a graph of `count` launches of an empty kernel of
+    the given launch shape: the fixed cost (dispatch, wave launch, drain) a
+    launch of that shape pays whatever it does."""
+    import torch
+
+    from lse_weighted_merge_dcp_amd import timing
+
+    def launch():
+        timing.empty_kernel(shape.blocks, shape.threads, torch.cuda.current_stream().cuda_stream)
+
+    us, _ = per_launch_us([launch] * count, reps=reps)
+    return us
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def trace_lookup(key, kernel, shape, nbytes):
+    """The committed rocprofv3 kernel-trace summary's figures for the launches
+    of this kernel at this launch shape (profiles/trace_<key>.json), while the
+    kernel sources still hash to what was traced; else None."""
+    p = os.path.join(ROOT, "profiles", "trace_%s.json" % key)
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source") != kernel_source_hash():
+        return None
+    fam = {"pack": "pack_", "combine": "combine_", "inplace": "inplace_"}[kernel]
+    for e in d.get("launch_shapes", []):
+        if e["kernel"].startswith(fam) and e["blocks"] == shape.blocks and e["threads"] == shape.threads:
+            avg_us = e["avg_ns"] / 1e3
+            return {"file": "profiles/trace_%s.json" % key, "instance": e["kernel"], "launches": e["calls"],
+                    "avg_us": round(avg_us, 3), "achieved": round(nbytes / (avg_us * 1e-6) / 1e9, 1),
+                    "frac": round(nbytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "note": "rocprofv3 average over every launch of this kernel at this shape in the traced "
+                            "bench.py command (in-step, cold and hot replays)"}
+    return None
+
+
+def measure(wl, key, B, args, full):
+    """Every figure of one workload: the timed step, each kernel inside the
+    step and cold, the cold layer, the roofline of the dominant kernel, the
+    per-rank share against the empty-kernel floor, and (full) the
+    cache-resident step, the copy ceiling and the CPU oracle."""
+    import torch
+
+    restore = getattr(wl, "restore", None)
+    wall, step_ms = time_step(wl, args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    gbs = wl.step_bytes() / (wall / args.steps) / 1e9
+    layers = getattr(wl, "layers", 1)
+
+    reps = max(3, args.steps // 4)
+    in_step, spans = in_step_us(wl.named_step(), reps, restore=restore)
+    kinfo = {}
+    shapes = {}
+    for name, nbytes, launches in wl.kernels():
+        cold, _ = per_launch_us(launches, reps=reps, restore=restore)
+        us = in_step[name]
+        if restore:
+            restore()
+        shapes[name] = launch_shape_of(launches[0])
+        kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                       "cold_us_per_launch": cold, "cold_GBps": nbytes / (cold * 1e-6) / 1e9,
+                       "launch": [shapes[name].blocks, shapes[name].threads]}
+    # every kernel of a layer run cold, one after the other: no layer's
+    # inputs left in the caches by the kernel before it
+    cold_us = sum(v["cold_us_per_launch"] for v in kinfo.values())
+    layer_bytes = wl.step_bytes() // layers
+    cold_layer = {"us": round(cold_us, 3), "GBps": round(layer_bytes / (cold_us * 1e-6) / 1e9, 1),
+                  "pct_of_hbm_peak": round(100.0 * layer_bytes / (cold_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                  "note": "sum of each kernel's cold per-launch time (its launches back to back on distinct "
+                          "buffers), free of data a previous kernel left in the Infinity Cache"}
+    dom = max(kinfo, key=lambda k: kinfo[k]["us_per_launch"])
+    achieved = kinfo[dom]["GBps"]
+    ckey = counter_key(key, B)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(ckey, wl, dom),
+                "timing": "inside the step: events on the kernel's own dispatches in eager replays of the step "
+                          "(one kernel timed per replay)",
+                "cold_achieved": round(kinfo[dom]["cold_GBps"], 1),
+                "cold_frac": round(kinfo[dom]["cold_GBps"] / PEAK_HBM_GBS, 4),
+                "trace": trace_lookup(ckey, dom, shapes[dom], kinfo[dom]["bytes_per_launch"])}
+    res = {
+        "value": round(gbs, 1),
+        "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_layer": round(ms_per_step * 1e3 / layers, 3),
+        "step_ms": percentiles(step_ms),
+        "bytes_per_step": wl.step_bytes(),
+        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                    for k, v in kinfo.items()},
+        "cold_layer": cold_layer,
+        "roofline": roofline,
+        "timed_replay_span_ms": spans,
+    }
+    if hasattr(wl, "per_rank"):
+        pr = {}
+        for name, nbytes, launches in wl.per_rank():
+            us, _ = per_launch_us(launches, reps=reps, restore=restore)
+            if restore:
+                restore()
+            shp = launch_shape_of(launches[0])
+            floor = empty_floor_us(shp, len(launches), reps)
+            pr[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
+                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "launch": [shp.blocks, shp.threads], "empty_kernel_us": round(floor, 3),
+                        "net_GBps": round(nbytes / (max(us - floor, 1e-3) * 1e-6) / 1e9, 1),
+                        "net_frac": round(nbytes / (max(us - floor, 1e-3) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        if hasattr(wl, "hot_launches"):
+            pr["us_per_layer"] = round(sum(v["us_per_launch"] for v in pr.values()), 3)
+        pr["note"] = ("one rank's / one destination's own call at its real shape, cold; empty_kernel_us is a "
+                      "graph of as many launches of an empty kernel with the same launch shape, net_GBps the "
+                      "rate net of that fixed cost")
+        res["per_rank"] = pr
+    if full:
+        if hasattr(wl, "hot_launches"):
+            us, _ = per_launch_us(wl.hot_launches(), reps=reps)
+            res["hot"] = {"us_per_layer": round(2 * us, 3),
+                          "GBps": round(wl.bytes_layer / (2 * us * 1e-6) / 1e9, 1),
+                          "note": "one layer's buffers reused by all layers (cache-resident)"}
+        ceilings = copy_ceiling_gbs(wl.dev)
+        ceiling = max(ceilings.values())
+        res["copy_ceiling_GBps"] = round(ceiling, 1)
+        res["copy_ceilings_GBps"] = {k: round(v, 1) for k, v in ceilings.items()}
+        res["pct_of_copy_ceiling"] = round(100.0 * gbs / ceiling, 2)
+        if args.cpu_budget > 0:
+            # the oracle on every host thread, then on one (a shorter sample)
+            from oracle import oracle as orc
+
+            cpu = wl.cpu_sample(args.cpu_budget)
+            n_all = orc.num_threads()
+            orc.set_num_threads(1)
+            one = wl.cpu_sample(max(1.0, args.cpu_budget / 3))
+            orc.set_num_threads(n_all)
+            cpu["cpu_model"] = cpu_model()
+            cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": one["cores"],
+                                  "sample": one["sample"]}
+            res["cpu_baseline"] = cpu
+        else:
+            res["cpu_baseline"] = None
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dsv3",
-                    choices=["dsv3", "longctx", "split", "tiny", "kimi", "kimi-rs", "dsv3fp8"])
+    ap.add_argument("--workload", default=None,
+                    choices=["dsv3", "longctx", "split", "tiny", "kimi", "kimi-rs", "dsv3fp8"],
+                    help="default: the long-context decode at B = 512, with dsv3 and kimi beside it")
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--layers", type=int, default=61)
+    ap.add_argument("--secondary", default=None,
+                    help="comma-separated workloads measured after the headline and reported under "
+                         "'secondary' (default: dsv3,kimi for the default run, none otherwise; 'none')")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--kv-len", action="store_true",
                     help="the pack reads per-rank KV lengths and neutralises tokens whose length is 0")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--summarize-counters", default=None)
+    ap.add_argument("--summarize-trace", default=None,
+                    help="rocprofv3 --kernel-trace --stats output directory -> profiles/trace_<key>.{json,md}")
     args = ap.parse_args()
 
+    default_run = args.workload is None
+    key = args.workload or HEADLINE[0]
+    B = args.B if args.B is not None or not default_run else HEADLINE[1]
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload, args.B)
+        summarize_counters(args.summarize_counters, key, B)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, key, B, command=os.environ.get("DCP_TRACE_COMMAND"))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -627,132 +877,40 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.workload == "kimi":
-        wl = InplaceWorkload(args.B, dev)
-    elif args.workload == "kimi-rs":
-        wl = ReduceScatterWorkload(args.B, dev)
-    else:
-        wl = A2AWorkload(args.workload, args.B, args.layers, dev, kv=args.kv_len)
-
+    wl = make_workload(key, B, args.layers, dev, kv=args.kv_len)
     if args.counter_run:
         counter_run(wl)
         return
 
-    # ---- the step: all layers, captured once in a HIP graph ----------------
-    if args.workload == "kimi":
-        step = [wl.run]
-        restore = wl.restore
-    elif args.workload == "kimi-rs":
-        step = [wl.run]
-        restore = None
-    else:
-        step = wl.step_launches()
-        restore = None
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(max(args.warmup, 1)):
-            if restore:
-                restore()
-            for f in step:
-                f()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for f in step:
-            f()
-    for _ in range(args.warmup):
-        if restore:
-            restore()
-        graph.replay()
-    torch.cuda.synchronize()
+    head = measure(wl, key, B, args, full=True)
+    config = wl.config()
+    del wl
+    torch.cuda.empty_cache()
 
-    # timed region: exactly K steps, synchronised on both sides
-    # (HIP events between the replays give the per-step spread)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    if restore is None:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            ev[2 * i].record()
-            graph.replay()
-            ev[2 * i + 1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        # the in-place call destroys its input: restore it (untimed) before each step
-        wall = 0.0
-        for i in range(args.steps):
-            restore()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            ev[2 * i].record()
-            graph.replay()
-            ev[2 * i + 1].record()
-            torch.cuda.synchronize()
-            wall += time.perf_counter() - t0
-    step_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
-    ms_per_step = wall / args.steps * 1e3
-    gbs = wl.step_bytes() / (wall / args.steps) / 1e9
-
-    # ---- per-kernel durations: inside the step (events on the kernels' own
-    # dispatches), and cold (HIP events around a replayed graph of that
-    # kernel's launches back to back)
-    reps = max(3, args.steps // 4)
-    in_step, spans = in_step_us(wl.named_step(), reps, restore=restore)
-    kinfo = {}
-    for name, nbytes, launches in wl.kernels():
-        cold, _ = per_launch_us(launches, reps=reps, restore=restore)
-        us = in_step[name]
-        kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
-                       "cold_us_per_launch": cold, "cold_GBps": nbytes / (cold * 1e-6) / 1e9}
-    extra = {}
-    layers = getattr(wl, "layers", 1)
-    if hasattr(wl, "per_rank"):
-        pr = {}
-        for name, nbytes, launches in wl.per_rank():
-            us, _ = per_launch_us(launches, reps=reps, restore=restore)
-            pr[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
-                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
-        if hasattr(wl, "hot_launches"):
-            pr["us_per_layer"] = round(sum(v["us_per_launch"] for v in pr.values()), 3)
-        extra["per_rank"] = pr
-    if hasattr(wl, "hot_launches"):
-        us, _ = per_launch_us(wl.hot_launches(), reps=reps)
-        extra["hot"] = {"us_per_layer": round(2 * us, 3),
-                        "GBps": round(wl.bytes_layer / (2 * us * 1e-6) / 1e9, 1),
-                        "note": "one layer's buffers reused by all layers (cache-resident)"}
-    ceilings = copy_ceiling_gbs(dev)
-    ceiling = max(ceilings.values())
-    dom = max(kinfo, key=lambda k: kinfo[k]["us_per_launch"])
-    achieved = kinfo[dom]["GBps"]
-    traffic = load_traffic(counter_key(args.workload, args.B), wl, dom)
-
-    cpu = None
-    if args.cpu_budget > 0:
-        # the oracle on every host thread, then on one (a shorter sample)
-        from oracle import oracle as orc
-
-        cpu = wl.cpu_sample(args.cpu_budget)
-        n_all = orc.num_threads()
-        orc.set_num_threads(1)
-        one = wl.cpu_sample(max(1.0, args.cpu_budget / 3))
-        orc.set_num_threads(n_all)
-        cpu["single_core"] = {"value": one["value"], "unit": one["unit"], "cores": one["cores"],
-                              "sample": one["sample"]}
+    secondary = {}
+    names = args.secondary
+    if names is None:
+        names = ",".join(DEFAULT_SECONDARY) if default_run else "none"
+    for sk in [n for n in names.split(",") if n and n != "none"]:
+        print("# secondary workload %s" % sk, file=sys.stderr, flush=True)
+        w2 = make_workload(sk, None, args.layers, dev)
+        r2 = measure(w2, sk, None, args, full=False)
+        r2 = {"config": w2.config(), "unit": "GB/s", **r2}
+        secondary[sk] = r2
+        del w2
+        torch.cuda.empty_cache()
 
     props = torch.cuda.get_device_properties(dev)
     device = {"arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
               "memory_bytes": props.total_memory}
     res = {
         "metric": METRIC,
-        "value": round(gbs, 1),
+        "value": head.pop("value"),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -761,25 +919,9 @@ def main():
         # itself is config.payload_dtype
         "dtype": "f32",
         "data": "synthetic",
-        "config": wl.config(),
-        "pct_of_hbm_peak": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "us_per_layer": round(ms_per_step * 1e3 / layers, 3),
-        "step_ms": percentiles(step_ms),
-        "copy_ceiling_GBps": round(ceiling, 1),
-        "copy_ceilings_GBps": {k: round(v, 1) for k, v in ceilings.items()},
-        "pct_of_copy_ceiling": round(100.0 * gbs / ceiling, 2),
-        "bytes_per_step": wl.step_bytes(),
-        "kernels": {k: {kk: round(vv, 3) if isinstance(vv, float) else vv for kk, vv in v.items()}
-                    for k, v in kinfo.items()},
-        **extra,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "timing": "inside the step: events on the kernel's own dispatches in eager replays of "
-                               "the step (one kernel timed per replay)",
-                     "cold_achieved": round(kinfo[dom]["cold_GBps"], 1),
-                     "cold_frac": round(kinfo[dom]["cold_GBps"] / PEAK_HBM_GBS, 4)},
-        "timed_replay_span_ms": spans,
-        "cpu_baseline": cpu,
+        "config": config,
+        **head,
+        "secondary": secondary,
         "kernel_source": kernel_source_hash(),
         "device": device,
     }
@@ -922,6 +1064,88 @@ def counters_markdown(d, directory):
             "%.3f" % (v["hbm_bytes_per_launch"] / a) if a else "-"))
     lines.append("")
     return "\n".join(lines)
+
+
+def _short_kernel_name(name):
+    """'void dcp::(anonymous namespace)::pack_stream_kernel<1, 8, true, false>(dcp::...)' ->
+    'pack_stream_kernel<1, 8, true, false>'."""
+    n = name.replace("dcp::(anonymous namespace)::", "").replace("dcp::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def summarize_trace(directory, workload, B=None, command=None):
+    """rocprofv3 --kernel-trace --stats output (run_kernel_stats.csv and
+    run_kernel_trace.csv under `directory`) -> profiles/trace_<key>.json and
+    .md: every library kernel's launches grouped by instance and launch shape
+    (workgroups x threads), with calls and average / min / max duration, and
+    rocprofv3's own per-instance statistics.  bench.py reads the JSON back to
+    set the traced average beside its own in-step figure."""
+    import csv
+
+    def find(suffix):
+        hits = glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)
+        if not hits:
+            raise SystemExit("no %s under %s" % (suffix, directory))
+        return hits[0]
+
+    stats = list(csv.DictReader(open(find("kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(find("kernel_trace.csv"))))
+    groups = {}
+    for r in trace:
+        name = _short_kernel_name(r["Kernel_Name"])
+        if not re.match(r"(pack_|combine_|inplace_|empty_kernel)", name):
+            continue
+        threads = int(r["Workgroup_Size_X"])
+        blocks = int(r["Grid_Size_X"]) // max(threads, 1)
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        groups.setdefault((name, blocks, threads), []).append(dur)
+    shapes = []
+    for (name, blocks, threads), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        shapes.append({"kernel": name, "blocks": blocks, "threads": threads, "calls": len(ds),
+                       "avg_ns": sum(ds) / len(ds), "min_ns": min(ds), "max_ns": max(ds), "total_ns": sum(ds)})
+    per_instance = []
+    for r in stats:
+        per_instance.append({"kernel": _short_kernel_name(r["Name"]), "calls": int(r["Calls"]),
+                             "avg_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]),
+                             "max_ns": float(r["MaxNs"]), "percentage": float(r["Percentage"])})
+    key = counter_key(workload, B)
+    out = {"kernel_source": kernel_source_hash(), "workload": workload, "key": key,
+           "command": command, "launch_shapes": shapes, "stats": per_instance}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "trace_%s.json" % key), "w") as fo:
+        json.dump(out, fo, indent=1)
+    lines = ["# Kernel trace: %s" % key, "",
+             "Kernel source hash `%s` (`trace_%s.json`; bench.py reads it back for `roofline.trace`" % (
+                 out["kernel_source"], key),
+             "while the kernel sources still hash to it).", ""]
+    if command:
+        lines += ["Command:", "", "```", command, "```", ""]
+    lines += ["rocprofv3 statistics (`kernel_stats.csv`, every launch of each instance, ns):", "",
+              "| Kernel | Calls | Average ns | Min ns | Max ns | Share |", "|---|---|---|---|---|---|"]
+    for e in per_instance:
+        lines.append("| `%s` | %d | %s | %s | %s | %.1f%% |" % (
+            e["kernel"], e["calls"], "{:,.0f}".format(e["avg_ns"]), "{:,.0f}".format(e["min_ns"]),
+            "{:,.0f}".format(e["max_ns"]), e["percentage"]))
+    lines += ["", "The library's launches by launch shape (`kernel_trace.csv`):", "",
+              "| Kernel | Workgroups x threads | Calls | Average ns | Min ns | Max ns |", "|---|---|---|---|---|---|"]
+    for e in shapes:
+        lines.append("| `%s` | %d x %d | %d | %s | %s | %s |" % (
+            e["kernel"], e["blocks"], e["threads"], e["calls"], "{:,.0f}".format(e["avg_ns"]),
+            "{:,}".format(e["min_ns"]), "{:,}".format(e["max_ns"])))
+    lines.append("")
+    with open(os.path.join(ROOT, "profiles", "trace_%s.md" % key), "w") as fo:
+        fo.write("\n".join(lines))
+    print(json.dumps({"key": key, "launch_shapes": shapes[:8]}, indent=1))
 
 
 def _fmt_bytes(x):

@@ -10,12 +10,15 @@
 static_assert(DCPB_ERR_CAPTURE == dcp::kStatusCapture, "capture status");
 
 namespace {
-dcp::CallTiming events(void* start_event, void* stop_event) {
+dcp::CallTiming events(void* start_event, void* stop_event, int64_t* shape) {
     dcp::CallTiming t;
     t.start = (hipEvent_t)start_event;
     t.stop = (hipEvent_t)stop_event;
+    t.shape = shape;
     return t;
 }
+
+__global__ __launch_bounds__(1024) void empty_kernel() {}
 }  // namespace
 
 extern "C" {
@@ -27,8 +30,8 @@ int dcpb_pack(void* start_event, void* stop_event,
               float* dst_lse, int64_t dl_R, int64_t dl_N, int64_t dl_B, int64_t dl_H,
               const int32_t* kv_len, int64_t kl_R, int64_t kl_B,
               int64_t R, int64_t N, int64_t B, int64_t H, int64_t D,
-              int dtype, void* stream) {
-    dcp::CallTiming t = events(start_event, stop_event);
+              int dtype, void* stream, int64_t* launch_shape) {
+    dcp::CallTiming t = events(start_event, stop_event, launch_shape);
     return dcp::pack_call(src_o, so_R, so_B, so_H, src_lse, sl_R, sl_B, sl_H, dst_o, do_R, do_N, do_B, do_H,
                           dst_lse, dl_R, dl_N, dl_B, dl_H, kv_len, kl_R, kl_B, R, N, B, H, D, dtype, stream, &t);
 }
@@ -39,8 +42,8 @@ int dcpb_unpack_combine(void* start_event, void* stop_event,
                         void* out, int64_t oo_R, int64_t oo_B, int64_t oo_H,
                         float* out_lse, int64_t ol_R, int64_t ol_B, int64_t ol_H,
                         int64_t R, int64_t N, int64_t B, int64_t Hpr, int64_t D,
-                        int dtype, int lse_base, void* stream) {
-    dcp::CallTiming t = events(start_event, stop_event);
+                        int dtype, int lse_base, void* stream, int64_t* launch_shape) {
+    dcp::CallTiming t = events(start_event, stop_event, launch_shape);
     return dcp::combine_call(recv_o, ro_R, ro_N, ro_B, ro_H, recv_lse, rl_R, rl_N, rl_B, rl_H, out, oo_R, oo_B,
                              oo_H, out_lse, ol_R, ol_B, ol_H, R, N, B, Hpr, D, dtype, lse_base, stream, &t);
 }
@@ -53,10 +56,18 @@ int dcpb_lse_combine_inplace(void* start_event, void* stop_event,
                              float* out_lse, int64_t ol_T, int64_t ol_H,
                              int64_t N, int64_t P, int64_t rank0,
                              int64_t T, int64_t H, int64_t D,
-                             int dtype, int lse_base, void* stream) {
-    dcp::CallTiming t = events(start_event, stop_event);
+                             int dtype, int lse_base, void* stream, int64_t* launch_shape) {
+    dcp::CallTiming t = events(start_event, stop_event, launch_shape);
     return dcp::inplace_call(partial, p_N, p_T, p_H, lse, l_N, l_T, l_H, h0, h1, out, o_T, o_H, out_lse, ol_T,
                              ol_H, N, P, rank0, T, H, D, dtype, lse_base, stream, &t);
+}
+
+int dcpb_empty_kernel(int64_t blocks, int threads, void* stream) {
+    if (blocks < 1 || blocks > (int64_t(1) << 31) - 1 || threads < 1 || threads > 1024) return -2;
+    void* args[] = {nullptr};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(empty_kernel), dim3((uint32_t)blocks),
+                                         dim3((uint32_t)threads), args, 0, (hipStream_t)stream);
+    return e == hipSuccess ? 0 : -9;
 }
 
 }  // extern "C"

@@ -29,7 +29,7 @@ BENCH_LIB = os.path.join(PKG, "libdcpmerge_bench.so")
 # exported names of each library (everything else is local)
 EXPORTS = {
     LIB: ["dcp_lse_pack_dim", "dcp_status_str", "dcp_pack", "dcp_unpack_combine", "dcp_lse_combine_inplace"],
-    BENCH_LIB: ["dcpb_pack", "dcpb_unpack_combine", "dcpb_lse_combine_inplace"],
+    BENCH_LIB: ["dcpb_pack", "dcpb_unpack_combine", "dcpb_lse_combine_inplace", "dcpb_empty_kernel"],
 }
 OBJECTS = {
     LIB: ["api", "pack", "combine", "inplace"],

@@ -21,6 +21,7 @@ constexpr int dtype_esize(int dt) {
 struct CallTiming {
     hipEvent_t start = nullptr;
     hipEvent_t stop = nullptr;
+    int64_t* shape = nullptr;   // nullable: [launches, workgroups of the last, threads per workgroup]
 };
 
 // Pack (and the plain strided row copy the N == 1 shortcuts use):
@@ -88,6 +89,11 @@ template <typename Arg>
 inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream, const Arg& arg,
                                 CallTiming* t) {
     void* args[] = {const_cast<Arg*>(&arg)};
+    if (t != nullptr && t->shape != nullptr) {
+        t->shape[0] += 1;
+        t->shape[1] = grid.x;
+        t->shape[2] = block.x;
+    }
     if (t == nullptr || (t->start == nullptr && t->stop == nullptr))
         return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
     hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream, t->start,

@@ -19,6 +19,7 @@ import os
 
 from . import _lib
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 BENCH_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcpmerge_bench.so")
 DCPB_ERR_CAPTURE = -10
 _bench = None
@@ -44,23 +45,54 @@ def bench_lib():
         for name in ("dcp_pack", "dcp_unpack_combine", "dcp_lse_combine_inplace"):
             args, res = _lib.SIGNATURES[name]
             fn = getattr(h, "dcpb_" + name[len("dcp_"):])
-            fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + list(args)
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + list(args) + [ctypes.c_void_p]
             fn.restype = res
+        h.dcpb_empty_kernel.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+        h.dcpb_empty_kernel.restype = ctypes.c_int
         _bench = h
     return _bench
 
 
-def call_timed(name: str, args: tuple, start: "Event | None", stop: "Event | None") -> int:
+class LaunchShape:
+    """What a call launched: launches, workgroups of its last launch and
+    threads per workgroup (filled by a call given timing=(None, None, shape))."""
+
+    def __init__(self):
+        self.buf = (ctypes.c_int64 * 3)(0, 0, 0)
+
+    @property
+    def launches(self) -> int:
+        return int(self.buf[0])
+
+    @property
+    def blocks(self) -> int:
+        return int(self.buf[1])
+
+    @property
+    def threads(self) -> int:
+        return int(self.buf[2])
+
+
+def call_timed(name: str, args: tuple, start: "Event | None", stop: "Event | None",
+               shape: "LaunchShape | None" = None) -> int:
     """Run libdcpmerge's `name` with the marshalled `args` through its timed
     twin dcpb_*; returns the status of include/dcpmerge.h (raises
-    CaptureError for DCPB_ERR_CAPTURE)."""
+    CaptureError for DCPB_ERR_CAPTURE).  `shape` receives what was launched."""
     fn = getattr(bench_lib(), "dcpb_" + name[len("dcp_"):])
-    st = fn(None if start is None else start.handle, None if stop is None else stop.handle, *args)
+    st = fn(None if start is None else start.handle, None if stop is None else stop.handle, *args,
+            None if shape is None else ctypes.cast(shape.buf, ctypes.c_void_p))
     if st == DCPB_ERR_CAPTURE:
         raise CaptureError(name)
     return st
 
-HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+def empty_kernel(blocks: int, threads: int, stream) -> None:
+    """Launch a kernel that does nothing, of `blocks` workgroups of `threads`
+    threads, on `stream` (a hipStream_t as an int, e.g. torch's cuda_stream)."""
+    st = bench_lib().dcpb_empty_kernel(int(blocks), int(threads), stream)
+    if st != 0:
+        raise RuntimeError("dcpb_empty_kernel failed with status %d" % st)
+
 
 _hip = None
 

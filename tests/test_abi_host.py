@@ -66,11 +66,35 @@ def test_bench_library_exports_exactly_its_timed_calls():
     from lse_weighted_merge_dcp_amd import timing
 
     declared = declared_in(BENCH_HEADER, "dcpb_")
-    assert declared == ["dcpb_lse_combine_inplace", "dcpb_pack", "dcpb_unpack_combine"]
+    assert declared == ["dcpb_empty_kernel", "dcpb_lse_combine_inplace", "dcpb_pack", "dcpb_unpack_combine"]
     assert exported_functions(timing.BENCH_LIB_PATH) == declared
     lib = timing.bench_lib()
-    for name in declared:
-        assert len(getattr(lib, name).argtypes) == len(_lib.SIGNATURES["dcp_" + name[5:]][0]) + 2
+    for name in declared[1:]:
+        assert len(getattr(lib, name).argtypes) == len(_lib.SIGNATURES["dcp_" + name[5:]][0]) + 3
+    assert lib.dcpb_empty_kernel(0, 64, None) == SHAPE and lib.dcpb_empty_kernel(1, 2048, None) == SHAPE
+
+
+def test_timing_module_names():
+    """Every name the timing module uses at run time is defined (its GPU
+    paths only run on the GPU machine)."""
+    import ast
+    import builtins
+
+    from lse_weighted_merge_dcp_amd import timing
+
+    tree = ast.parse(open(timing.__file__).read())
+    defined = set(dir(timing)) | set(dir(builtins))
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.FunctionDef, ast.Lambda)):
+            for a in node.args.args + node.args.kwonlyargs:
+                defined.add(a.arg)
+        if isinstance(node, ast.Name) and isinstance(node.ctx, ast.Store):
+            defined.add(node.id)
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+            defined.add(node.name)
+    used = {n.id for n in ast.walk(tree) if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load)}
+    assert used <= defined, sorted(used - defined)
+    assert timing.HIP_EVENT_DISABLE_SYSTEM_FENCE == 0x20000000
 
 
 def test_bench_library_validates_like_the_library():
@@ -82,10 +106,13 @@ def test_bench_library_validates_like_the_library():
     args = list(dict(src_o=A, so_R=0, so_B=512, so_H=64, src_lse=A, sl_R=0, sl_B=8, sl_H=1,
                      dst_o=A, do_R=0, do_N=256, do_B=128, do_H=64, dst_lse=A, dl_R=0, dl_N=4, dl_B=2, dl_H=1,
                      kv_len=None, kl_R=0, kl_B=1, R=1, N=3, B=4, H=8, D=64, dtype=0, stream=None).values())
-    assert lib.dcpb_pack(A, A + 256, *args) == HEADS          # N = 3 does not divide H = 8
+    assert lib.dcpb_pack(A, A + 256, *args, None) == HEADS    # N = 3 does not divide H = 8
     assert _lib.lib().dcp_pack(*args) == HEADS
     args[-6], args[-5] = 2, 0                                  # N = 2, B = 0: a valid no-op
-    assert lib.dcpb_pack(A, A + 256, *args) == OK
+    shape = timing.LaunchShape()
+    import ctypes
+    assert lib.dcpb_pack(A, A + 256, *args, ctypes.cast(shape.buf, ctypes.c_void_p)) == OK
+    assert shape.launches == 0
     assert _lib.lib().dcp_pack(*args) == OK
 
 

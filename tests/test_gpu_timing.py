@@ -79,6 +79,19 @@ def test_start_or_stop_alone():
     assert a.elapsed_us(b) > 0
 
 
+def test_launch_shape_of_a_call():
+    """A call given a shape record reports what it launched; an empty
+    kernel of that shape runs."""
+    say("launch shape")
+    _, _, o, l = inputs()
+    send, pay, words = send_buffers()
+    shape = timing.LaunchShape()
+    ops.dcp_pack_a2a_send(o, l, pay, words, timing=(None, None, shape))
+    assert shape.launches == 1 and shape.blocks >= 1 and shape.threads in (64, 128, 256, 512)
+    timing.empty_kernel(shape.blocks, shape.threads, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+
 def test_call_without_launch_records_nothing():
     say("zero-sized call")
     _, _, o, l = inputs()
@@ -98,7 +111,7 @@ def test_rejected_call_records_nothing():
     s, e = timing.Event(), timing.Event()
     st = timing.bench_lib().dcpb_pack(s.handle, e.handle, o.data_ptr(), 0, 0, 0, l.data_ptr(), 0, 0, 0,
                                       pay.data_ptr(), 0, 0, 0, 0, words.data_ptr(), 0, 0, 0, 0,
-                                      None, 0, 0, 1, N, B, H, D, 7, None)
+                                      None, 0, 0, 1, N, B, H, D, 7, None, None)
     assert _lib.STATUS[st] == "DCP_ERR_DTYPE"
     ops.dcp_pack_a2a_send(o, l, pay, words)
     torch.cuda.synchronize()
