@@ -160,9 +160,21 @@ constexpr int64_t kStreamWide = 32768;
 // costs 3% (the DeepSeek-V3-shaped pack, 67 MB of source).
 constexpr int64_t kStreamNtSourceBytes = int64_t(96) << 20;
 
+// Calls whose send blocks span at least this many bytes (three times the
+// 256 MB Infinity Cache) write them with the nontemporal hint.  Below it
+// part of the send buffer is still cached when the combine reads it, and
+// that is worth more than faster stores (measured on MI355X, long-context
+// decode, 61 layers: B = 512, 1.08 GB of send blocks, step 5,706 -> 5,857
+// GB/s, the pack 375 -> 363 us inside the step and 398 -> 362 us cold, the
+// combine unchanged; B = 256, 539 MB, step 6,188 -> 5,840 GB/s, its combine
+// 95.9 -> 104.6 us; B = 64 -8%).
+constexpr int64_t kStreamNtDestBytes = int64_t(768) << 20;
+
 // TWO: rows of 512 to 1020 bytes, where a wave-step can hold a second LSE
-// word; rows of 1 KB and more keep the one-LSE form.
-template <int U, int WPB, bool NTL, bool TWO>
+// word; rows of 1 KB and more keep the one-LSE form.  NTS: send blocks
+// written with the nontemporal hint (a compile-time choice: with a runtime
+// flag the compiler merges the two stores into one plain store).
+template <int U, int WPB, bool NTL, bool TWO, bool NTS>
 __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
@@ -229,7 +241,7 @@ __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) 
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (on[u]) vstore<16>(dp[u], v[u]);
+        if (on[u]) vstore_out<16, NTS>(dp[u], v[u]);
 }
 
 // True when dst/dst_lse form a peer-outer interleaved buffer whose blocks the
@@ -248,15 +260,18 @@ bool stream_layout(const PackArgs& a) {
 }
 
 template <bool TWO>
-hipError_t launch_stream(const StreamK& k, bool nt_source, hipStream_t stream, CallTiming* t) {
+hipError_t launch_stream(const StreamK& k, bool nt_source, bool nt_dest, hipStream_t stream, CallTiming* t) {
     if (k.nsteps >= kStreamWide) {
         const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
+        if (nt_dest)
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, true>, dim3(blocks), dim3(512), stream, k, t);
         if (nt_source)
-            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO>, dim3(blocks), dim3(512), stream, k, t);
-        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO>, dim3(blocks), dim3(512), stream, k, t);
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, false>, dim3(blocks), dim3(512), stream, k,
+                                 t);
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO, false>, dim3(blocks), dim3(512), stream, k, t);
     }
     const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO>, dim3(blocks), dim3(256), stream, k, t);
+    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO, false>, dim3(blocks), dim3(256), stream, k, t);
 }
 
 hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
@@ -269,6 +284,7 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
     int64_t r_chunk = lim / per_r;
     int64_t b_chunk = a.B;
     const bool nt_source = a.R * a.B * a.H * a.row_bytes >= kStreamNtSourceBytes;
+    const bool nt_dest = a.R * a.B * a.H * W >= kStreamNtDestBytes;
     if (r_chunk < 1) {
         r_chunk = 1;
         b_chunk = lim / (N * S);
@@ -297,8 +313,8 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.f_N = make_fastdiv(k.N);
             k.f_B = make_fastdiv(k.B);
             k.f_Wd = make_fastdiv(k.Wd);
-            const hipError_t e = k.Wd < 256 ? launch_stream<true>(k, nt_source, stream, a.timing)
-                                             : launch_stream<false>(k, nt_source, stream, a.timing);
+            const hipError_t e = k.Wd < 256 ? launch_stream<true>(k, nt_source, nt_dest, stream, a.timing)
+                                             : launch_stream<false>(k, nt_source, nt_dest, stream, a.timing);
             if (e != hipSuccess) return e;
         }
     }

@@ -72,6 +72,33 @@ def test_pack_interleaved_workloads(key, B):
     assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
 
 
+def test_pack_large_send_blocks_fp8_two_lse_words():
+    """A pack whose send blocks span 768 MiB or more writes them with the
+    nontemporal hint; fp8 rows of 516 bytes (two LSE words in most
+    wave-steps) at 811 MB, compared byte for byte with guard bands."""
+    N, B, H, D, dt = 16, 768, 128, 512, "fp8"
+    Hpr = H // N
+    say("pack large fp8", N, B, H, D)
+    g = torch.Generator().manual_seed(5)
+    out = synth.to_storage(torch.randn(N, B, H, D, generator=g), dt)
+    lse = np.random.default_rng(5).normal(10, 3, size=(N, B, H)).astype(np.float32)
+    shape = (N, N, B, Hpr, D + 4)
+    nbytes = int(np.prod(shape))
+    assert nbytes >= 768 << 20
+    buf, host = guarded(nbytes, seed=17)
+    send = dev_view(buf, TORCH_DT[dt], shape)
+    pay, words = ops.interleaved_views(send, D)
+    ops.dcp_pack_a2a_send(to_dev(out, dt, DEV), torch.from_numpy(lse).to(DEV), pay, words)
+    got = buf.cpu().numpy()
+    hsend = host_view(host, NP_DT[dt], shape)
+    hpay, hwords = orc.interleaved_views_np(hsend, D, dt)
+    for r in range(N):
+        orc.pack(out[r], lse[r], hpay[r], hwords[r], N)
+    assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
+    del buf, send, pay, words
+    torch.cuda.empty_cache()
+
+
 STREAM_SHAPES = [
     ("bf16", 8, 5, 16, 512),    # the decode shape, ragged batch
     ("bf16", 4, 3, 4, 512),     # small peer blocks (Hpr * W = 4112 B)
