@@ -253,11 +253,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 // size.  Small launches
 // also use one-wave workgroups (WPB = 1): the rows then spread over up to
 // four times as many CUs, and each CU's load pipeline serves fewer of them.
+// Block order of the row-per-wave kernel: the XCDs take turns on chunks of
+// this many workgroups (1024 rows in 4-wave workgroups).  Grids of at most
+// 8 chunks (every launch of up to 2048 workgroups, such as one decode layer
+// of the DeepSeek-V3 shape) are XCD-contiguous.  Measured on MI355X against
+// the XCD-contiguous order of every launch: long-context B = 512 combine
+// (16,384 workgroups) 201 -> 180 us, B = 256 96.4 -> 93.3 us, the
+// Kimi-K3-shaped reduce-scatter merge 4.97-5.04 -> 4.85-4.92 ms.  (Chunks of
+// 512 gave 176 us at B = 512 but 4.95 ms on the reduce-scatter merge; chunks
+// that do not divide a destination's rows, such as 384 or 768 at B = 512,
+// were slower than either.)
+constexpr uint32_t kWaveChunk = 256;
+
 template <typename DT, int NT, bool HOIST, int WPB, bool NTS>
 __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     using C = Cvt<DT, 16>;
     constexpr int EPV = C::n;
-    const uint32_t blk = xcd_block();
+    const uint32_t blk = xcd_chunk_block<kWaveChunk>();
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t j = lane & 15u;

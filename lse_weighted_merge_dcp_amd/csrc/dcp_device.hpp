@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "block_order.hpp"
 #include "fastdiv.hpp"
 
 namespace dcp {
@@ -326,12 +327,11 @@ __device__ __forceinline__ float guard_f(float x) { return __builtin_isfinite(x)
 // i mod 8), and each XCD has its own L2.  Renumber blocks so that each XCD
 // walks one contiguous range of rows: neighbouring rows share cache lines at
 // their ends (interleaved rows are 4-byte aligned), and a line stays in one L2.
-__device__ __forceinline__ uint32_t xcd_block() {
-    const uint32_t n = gridDim.x, b = blockIdx.x;
-    const uint32_t xcd = b & 7u, k = b >> 3;
-    const uint32_t q = n >> 3, rem = n & 7u;
-    return xcd * q + (xcd < rem ? xcd : rem) + k;
-}
+__device__ __forceinline__ uint32_t xcd_block() { return xcd_contiguous_order(blockIdx.x, gridDim.x); }
+
+// The same with the XCDs taking turns on chunks of C blocks (block_order.hpp).
+template <uint32_t C>
+__device__ __forceinline__ uint32_t xcd_chunk_block() { return xcd_chunked_order<C>(blockIdx.x, gridDim.x); }
 
 __device__ __forceinline__ uint32_t wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

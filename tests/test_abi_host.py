@@ -281,6 +281,62 @@ def test_fastdiv_matches_integer_division(tmp_path):
     assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout
 
 
+BLOCK_ORDER_TEST = r"""
+#include <cstdio>
+#include <cstdint>
+#include <vector>
+#include "block_order.hpp"
+template <uint32_t C>
+long check(uint32_t n) {
+    std::vector<char> seen(n, 0);
+    long bad = 0;
+    for (uint32_t b = 0; b < n; ++b) {
+        const uint32_t l = dcp::xcd_chunked_order<C>(b, n);
+        if (l >= n || seen[l]) ++bad; else seen[l] = 1;
+    }
+    // a grid of at most 8 C blocks keeps the contiguous order
+    if (n <= 8 * C)
+        for (uint32_t b = 0; b < n; ++b) bad += dcp::xcd_chunked_order<C>(b, n) != dcp::xcd_contiguous_order(b, n);
+    return bad;
+}
+int main() {
+    long bad = 0;
+    std::vector<uint32_t> ns;
+    for (uint32_t n = 1; n <= 5000; ++n) ns.push_back(n);
+    for (uint32_t n : {8191u, 8192u, 8193u, 16384u, 16391u, 65536u, 786432u, 786439u, 1u << 21}) ns.push_back(n);
+    for (uint32_t n : ns) {
+        std::vector<char> seen(n, 0);
+        for (uint32_t b = 0; b < n; ++b) {
+            const uint32_t l = dcp::xcd_contiguous_order(b, n);
+            if (l >= n || seen[l]) ++bad; else seen[l] = 1;
+            // consecutive workgroups of one XCD take consecutive blocks
+            if (b >= 8 && l != dcp::xcd_contiguous_order(b - 8, n) + 1) ++bad;
+        }
+        bad += check<1>(n) + check<3>(n) + check<64>(n) + check<256>(n) + check<512>(n);
+    }
+    // inside whole rounds, XCD x's k-th workgroup is block k mod C of chunk (k / C) * 8 + x
+    for (uint32_t b = 0; b < 16384; ++b) {
+        const uint32_t x = b % 8, k = b / 8;
+        bad += dcp::xcd_chunked_order<256>(b, 16384) != ((k / 256) * 8 + x) * 256 + k % 256;
+    }
+    std::printf("%ld\n", bad);
+    return bad != 0;
+}
+"""
+
+
+def test_block_orders_are_bijections(tmp_path):
+    """The XCD-aware workgroup orders (csrc/block_order.hpp, the same code the
+    kernels run) map every grid of up to 5000 blocks, and larger ones of the
+    workloads' sizes, one to one onto its blocks."""
+    src = tmp_path / "bo.cpp"
+    src.write_text(BLOCK_ORDER_TEST)
+    exe = str(tmp_path / "bo")
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-I" + CSRC, str(src), "-o", exe])
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout
+
+
 def test_header_compiles_as_c_and_the_c_client_links(tmp_path):
     """include/dcpmerge.h is plain C: a C11 caller (tests/c_abi_client.c)
     compiles with -Wall -Wextra -Werror and links against libdcpmerge.so and

@@ -9,7 +9,8 @@ with every report fatal (-fno-sanitize-recover=all):
   size limits and the element-to-byte stride conversion) driven by
   tests/host_validation_fuzz.cpp with extreme and random arguments, the
   kernel launchers replaced by recording stubs (no GPU, no HIP runtime);
-* the fast division the kernels index with (csrc/fastdiv.hpp).
+* the fast division the kernels index with (csrc/fastdiv.hpp) and the
+  XCD-aware workgroup orders (csrc/block_order.hpp).
 """
 import os
 import subprocess
@@ -78,4 +79,16 @@ def test_fastdiv_under_asan_and_ubsan(tmp_path):
     exe = str(tmp_path / "fd")
     subprocess.check_call(["g++", "-std=c++17", "-I" + CSRC] + SAN + [str(src), "-o", exe])
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip() == "0", (r.stdout, r.stderr[-2000:])
+
+
+def test_block_orders_under_asan_and_ubsan(tmp_path):
+    from test_abi_host import BLOCK_ORDER_TEST
+
+    src = tmp_path / "bo.cpp"
+    src.write_text(BLOCK_ORDER_TEST)
+    exe = str(tmp_path / "bo")
+    subprocess.check_call(["g++", "-std=c++17", "-I" + CSRC] + SAN + [str(src), "-o", exe])
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600,
+                       env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1"))
     assert r.returncode == 0 and r.stdout.strip() == "0", (r.stdout, r.stderr[-2000:])
