@@ -472,9 +472,11 @@ def copy_ceiling_gbs(dev, nbytes=2 << 30, reps=10):
     moved = 2 * (nbytes + 4 * T)
     library = moved / _median_event_s(
         lambda: ops.dcp_lse_combine(src, lse, is_lse_base_on_e=True, out=out, out_lse=g), reps) / 1e9
+    shape = launch_shape_of(lambda **kw: ops.dcp_lse_combine(src, lse, is_lse_base_on_e=True, out=out, out_lse=g,
+                                                              **kw))
     del a, src, lse, out, g
     torch.cuda.empty_cache()
-    return {"runtime": runtime, "library_row_copy": library}
+    return {"runtime": runtime, "library_row_copy": library, "library_row_copy_launch": [shape.blocks, shape.threads]}
 
 
 def percentiles(xs):
@@ -707,24 +709,29 @@ def cpu_model():
 
 
 def trace_lookup(key, kernel, shape, nbytes):
-    """The committed rocprofv3 kernel-trace summary's figures for the launches
-    of this kernel at this launch shape (profiles/trace_<key>.json), while the
-    kernel sources still hash to what was traced; else None."""
-    p = os.path.join(ROOT, "profiles", "trace_%s.json" % key)
-    if not os.path.exists(p):
-        return None
-    d = json.load(open(p))
-    if d.get("kernel_source") != kernel_source_hash():
-        return None
+    """The committed rocprofv3 kernel-trace summaries' figures for the launches
+    of this kernel at this launch shape (profiles/trace_*.json, the one named
+    for this workload first), while the kernel sources still hash to what was
+    traced; else None."""
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "trace_*.json")))
+    own = os.path.join(ROOT, "profiles", "trace_%s.json" % key)
+    if own in paths:
+        paths.remove(own)
+        paths.insert(0, own)
     fam = {"pack": "pack_", "combine": "combine_", "inplace": "inplace_"}[kernel]
-    for e in d.get("launch_shapes", []):
-        if e["kernel"].startswith(fam) and e["blocks"] == shape.blocks and e["threads"] == shape.threads:
-            avg_us = e["avg_ns"] / 1e3
-            return {"file": "profiles/trace_%s.json" % key, "instance": e["kernel"], "launches": e["calls"],
-                    "avg_us": round(avg_us, 3), "achieved": round(nbytes / (avg_us * 1e-6) / 1e9, 1),
-                    "frac": round(nbytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                    "note": "rocprofv3 average over every launch of this kernel at this shape in the traced "
-                            "bench.py command (in-step, cold and hot replays)"}
+    src = kernel_source_hash()
+    for p in paths:
+        d = json.load(open(p))
+        if d.get("kernel_source") != src:
+            continue
+        for e in d.get("launch_shapes", []):
+            if e["kernel"].startswith(fam) and e["blocks"] == shape.blocks and e["threads"] == shape.threads:
+                avg_us = e["avg_ns"] / 1e3
+                return {"file": os.path.relpath(p, ROOT), "instance": e["kernel"], "launches": e["calls"],
+                        "avg_us": round(avg_us, 3), "achieved": round(nbytes / (avg_us * 1e-6) / 1e9, 1),
+                        "frac": round(nbytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "note": "rocprofv3 average over every launch of this kernel at this shape in the traced "
+                                "bench.py command (in-step, cold and hot replays)"}
     return None
 
 
@@ -812,6 +819,7 @@ def measure(wl, key, B, args, full):
                           "GBps": round(wl.bytes_layer / (2 * us * 1e-6) / 1e9, 1),
                           "note": "one layer's buffers reused by all layers (cache-resident)"}
         ceilings = copy_ceiling_gbs(wl.dev)
+        res["copy_ceiling_launch"] = ceilings.pop("library_row_copy_launch")
         ceiling = max(ceilings.values())
         res["copy_ceiling_GBps"] = round(ceiling, 1)
         res["copy_ceilings_GBps"] = {k: round(v, 1) for k, v in ceilings.items()}
@@ -864,7 +872,8 @@ def main():
         summarize_counters(args.summarize_counters, key, B)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, key, B, command=os.environ.get("DCP_TRACE_COMMAND"))
+        summarize_trace(args.summarize_trace, key, B, command=os.environ.get("DCP_TRACE_COMMAND"),
+                        bench_json=os.environ.get("DCP_TRACE_BENCH_JSON"))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1069,7 +1078,7 @@ def counters_markdown(d, directory):
 def _short_kernel_name(name):
     """'void dcp::(anonymous namespace)::pack_stream_kernel<1, 8, true, false>(dcp::...)' ->
     'pack_stream_kernel<1, 8, true, false>'."""
-    n = name.replace("dcp::(anonymous namespace)::", "").replace("dcp::", "")
+    n = name.replace("(anonymous namespace)::", "").replace("dcp::", "")
     if n.startswith("void "):
         n = n[5:]
     depth = 0
@@ -1083,7 +1092,37 @@ def _short_kernel_name(name):
     return n
 
 
-def summarize_trace(directory, workload, B=None, command=None):
+def _launch_roles(bench_json):
+    """{(family, workgroups, threads): role} from the JSON line of the traced
+    bench.py run (each kernel's and per-rank call's launch shape)."""
+    roles = {}
+    if not bench_json or not os.path.exists(bench_json):
+        return roles
+    with open(bench_json) as f:
+        line = [ln for ln in f if ln.startswith("{")][-1]
+    d = json.loads(line)
+
+    def add(res, wname):
+        for k, v in res.get("kernels", {}).items():
+            if "launch" in v:
+                roles.setdefault((k, v["launch"][0], v["launch"][1]), "%s, %s (every rank stacked)" % (wname, k))
+        for k, v in (res.get("per_rank") or {}).items():
+            if isinstance(v, dict) and "launch" in v:
+                roles.setdefault((k, v["launch"][0], v["launch"][1]), "%s, one rank's %s" % (wname, k))
+
+    add(d, d["config"]["workload"].split(":")[0])
+    for name, sec in d.get("secondary", {}).items():
+        add(sec, sec["config"]["workload"].split(":")[0])
+    if "copy_ceiling_launch" in d:
+        blocks, threads = d["copy_ceiling_launch"]
+        roles.setdefault(("pack", blocks, threads), "the library's 2 GiB row copy (copy ceiling)")
+    for (fam, blocks, threads), role in list(roles.items()):
+        if "one rank's" in role:
+            roles[("empty", blocks, threads)] = "empty kernel of the launch shape of " + role
+    return roles
+
+
+def summarize_trace(directory, workload, B=None, command=None, bench_json=None, out_dir=None):
     """rocprofv3 --kernel-trace --stats output (run_kernel_stats.csv and
     run_kernel_trace.csv under `directory`) -> profiles/trace_<key>.json and
     .md: every library kernel's launches grouped by instance and launch shape
@@ -1118,11 +1157,15 @@ def summarize_trace(directory, workload, B=None, command=None):
         per_instance.append({"kernel": _short_kernel_name(r["Name"]), "calls": int(r["Calls"]),
                              "avg_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]),
                              "max_ns": float(r["MaxNs"]), "percentage": float(r["Percentage"])})
+    roles = _launch_roles(bench_json)
+    for e in shapes:
+        e["role"] = roles.get((e["kernel"].split("_")[0], e["blocks"], e["threads"]), "")
     key = counter_key(workload, B)
     out = {"kernel_source": kernel_source_hash(), "workload": workload, "key": key,
            "command": command, "launch_shapes": shapes, "stats": per_instance}
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "trace_%s.json" % key), "w") as fo:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "trace_%s.json" % key), "w") as fo:
         json.dump(out, fo, indent=1)
     lines = ["# Kernel trace: %s" % key, "",
              "Kernel source hash `%s` (`trace_%s.json`; bench.py reads it back for `roofline.trace`" % (
@@ -1133,17 +1176,20 @@ def summarize_trace(directory, workload, B=None, command=None):
     lines += ["rocprofv3 statistics (`kernel_stats.csv`, every launch of each instance, ns):", "",
               "| Kernel | Calls | Average ns | Min ns | Max ns | Share |", "|---|---|---|---|---|---|"]
     for e in per_instance:
+        name = e["kernel"] if len(e["kernel"]) <= 100 else e["kernel"][:97] + "..."
         lines.append("| `%s` | %d | %s | %s | %s | %.1f%% |" % (
-            e["kernel"], e["calls"], "{:,.0f}".format(e["avg_ns"]), "{:,.0f}".format(e["min_ns"]),
+            name, e["calls"], "{:,.0f}".format(e["avg_ns"]), "{:,.0f}".format(e["min_ns"]),
             "{:,.0f}".format(e["max_ns"]), e["percentage"]))
-    lines += ["", "The library's launches by launch shape (`kernel_trace.csv`):", "",
-              "| Kernel | Workgroups x threads | Calls | Average ns | Min ns | Max ns |", "|---|---|---|---|---|---|"]
+    lines += ["", "The library's launches by launch shape (`kernel_trace.csv`; the role from the traced run's",
+              "own JSON line, which records each call's launch shape):", "",
+              "| Kernel | Workgroups x threads | Role | Calls | Average ns | Min ns | Max ns |",
+              "|---|---|---|---|---|---|---|"]
     for e in shapes:
-        lines.append("| `%s` | %d x %d | %d | %s | %s | %s |" % (
-            e["kernel"], e["blocks"], e["threads"], e["calls"], "{:,.0f}".format(e["avg_ns"]),
+        lines.append("| `%s` | %d x %d | %s | %d | %s | %s | %s |" % (
+            e["kernel"], e["blocks"], e["threads"], e["role"], e["calls"], "{:,.0f}".format(e["avg_ns"]),
             "{:,}".format(e["min_ns"]), "{:,}".format(e["max_ns"])))
     lines.append("")
-    with open(os.path.join(ROOT, "profiles", "trace_%s.md" % key), "w") as fo:
+    with open(os.path.join(out_dir, "trace_%s.md" % key), "w") as fo:
         fo.write("\n".join(lines))
     print(json.dumps({"key": key, "launch_shapes": shapes[:8]}, indent=1))
 

@@ -57,3 +57,48 @@ def test_fp8_bytes_and_counter_keys():
     assert bench.counter_key("dsv3") == "dsv3" and bench.counter_key("kimi-rs") == "kimi-rs"
     assert bench.counter_key("longctx", 64) == "longctx_B64"
     assert bench.counter_key("longctx") == "longctx_B512"
+
+
+def test_trace_summary_groups_launch_shapes_and_labels_them(tmp_path):
+    """--summarize-trace: rocprofv3's kernel CSVs -> per (instance, launch
+    shape) averages, labelled with the role the traced run's JSON line gives
+    each launch shape; bench.py finds its dominant kernel's entry again."""
+    import csv
+    import json
+
+    d = tmp_path / "prof"
+    d.mkdir()
+    pack = "void dcp::(anonymous namespace)::pack_stream_kernel<1, 8, true, false, true>(dcp::(anonymous namespace)::StreamK)"
+    comb = "void dcp::(anonymous namespace)::combine_wave_kernel<dcp::BF16T, 16, true, 4, true>(dcp::(anonymous namespace)::CombK)"
+    empty = "void (anonymous namespace)::empty_kernel()"
+    rows = [(pack, 100, 460, 512, 147456), (pack, 500, 840, 512, 147456), (pack, 0, 30, 512, 9216),
+            (comb, 1000, 1200, 256, 16384), (empty, 0, 5, 512, 9216),
+            ("void at::cuda::(anonymous namespace)::spin_kernel(long)", 0, 99, 1, 1)]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X"])
+        for name, t0, t1, wg, blocks in rows:
+            w.writerow([name, t0, t1, wg, wg * blocks])
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writerow([pack, 3, 263.3, 30, 360, 80.0])
+    line = {"config": {"workload": "long-context decode sweep: N=16"},
+            "kernels": {"pack": {"launch": [147456, 512]}, "combine": {"launch": [16384, 256]}},
+            "per_rank": {"pack": {"launch": [9216, 512]}, "note": "x"}, "secondary": {}}
+    bj = tmp_path / "bench.json"
+    bj.write_text("# a log line\n" + json.dumps(line) + "\n")
+    out = tmp_path / "out"
+    bench.summarize_trace(str(d), "longctx", None, command="cmd", bench_json=str(bj), out_dir=str(out))
+    t = json.load(open(out / "trace_longctx_B512.json"))
+    by = {(e["kernel"], e["blocks"]): e for e in t["launch_shapes"]}
+    p = by[("pack_stream_kernel<1, 8, true, false, true>", 147456)]
+    assert p["calls"] == 2 and p["avg_ns"] == 350 and p["min_ns"] == 340 and p["max_ns"] == 360
+    assert p["role"] == "long-context decode sweep, pack (every rank stacked)"
+    assert by[("pack_stream_kernel<1, 8, true, false, true>", 9216)]["role"] == "long-context decode sweep, one rank's pack"
+    assert by[("empty_kernel", 9216)]["role"].startswith("empty kernel of the launch shape of")
+    assert by[("combine_wave_kernel<BF16T, 16, true, 4, true>", 16384)]["avg_ns"] == 200
+    assert not any(e["kernel"].startswith("at::") for e in t["launch_shapes"])
+    assert t["stats"][0]["kernel"] == "pack_stream_kernel<1, 8, true, false, true>"
+    assert "| `pack_stream_kernel<1, 8, true, false, true>` | 147456 x 512 |" in (out / "trace_longctx_B512.md").read_text()
+    assert bench._short_kernel_name("void at::cuda::(anonymous namespace)::spin_kernel(long)") == "at::cuda::spin_kernel"
