@@ -1,5 +1,5 @@
-"""CPU builds under AddressSanitizer and UndefinedBehaviorSanitizer (gcc),
-with every report fatal (-fno-sanitize-recover=all):
+"""CPU builds under AddressSanitizer and UndefinedBehaviorSanitizer (gcc, and
+ROCm's clang for the HIP sources), with every report fatal (-fno-sanitize-recover=all):
 
 * the fp64 oracle (oracle/dcp_oracle.c) built with both sanitizers, and the
   oracle pins and the two-oracle agreement tests run against that build in a
@@ -9,6 +9,9 @@ with every report fatal (-fno-sanitize-recover=all):
   size limits and the element-to-byte stride conversion) driven by
   tests/host_validation_fuzz.cpp with extreme and random arguments, the
   kernel launchers replaced by recording stubs (no GPU, no HIP runtime);
+* the real kernel launchers (pack.hip, combine.hip, inplace.hip compiled for
+  the host only) behind the C ABI, driven by tests/host_launch_check.cpp
+  with random valid calls, every launch checked against the grid limits;
 * the fast division the kernels index with (csrc/fastdiv.hpp) and the
   XCD-aware workgroup orders (csrc/block_order.hpp).
 """
@@ -92,3 +95,47 @@ def test_block_orders_under_asan_and_ubsan(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600,
                        env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1"))
     assert r.returncode == 0 and r.stdout.strip() == "0", (r.stdout, r.stderr[-2000:])
+
+
+def _hipcc():
+    cand = os.path.join(ROCM, "bin", "hipcc")
+    if not os.path.exists(cand):
+        pytest.skip("hipcc is not here")
+    return cand
+
+
+def test_kernel_launches_under_asan_and_ubsan(tmp_path):
+    """The real launchers of pack.hip, combine.hip and inplace.hip and the C
+    ABI of api.cpp, compiled for the host only (an empty device binary stands
+    in for the gfx950 code) with ASan and UBSan, driven by
+    tests/host_launch_check.cpp: random valid calls from tiny to far beyond
+    one launch's reach, every launch checked against the grid limits."""
+    clangxx = os.path.join(ROCM, "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clangxx):
+        pytest.skip("ROCm's clang++ is not here")
+    fatbin = tmp_path / "empty.fatbin"
+    fatbin.write_bytes(b"")
+    host_only = [_hipcc(), "-x", "hip", "--cuda-host-only", "-std=c++20", "-O1", "-g", "-w",
+                 "-I" + os.path.join(ROOT, "include"),
+                 "-Xarch_host", "-fsanitize=address,undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all",
+                 "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xclang", "-fcuda-include-gpubinary", "-Xclang", str(fatbin), "-c"]
+    srcs = [os.path.join(CSRC, f) for f in ("api.cpp", "pack.hip", "combine.hip", "inplace.hip")]
+    srcs.append(os.path.join(ROOT, "tests", "host_launch_check.cpp"))
+    objs = []
+    for src in srcs:
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        subprocess.check_call(host_only + [src, "-o", obj])
+        objs.append(obj)
+    exe = str(tmp_path / "host_launch_check")
+    # no HIP runtime is linked: the check program defines the few entry points the launchers call
+    subprocess.check_call([clangxx, "-fsanitize=address,undefined", "-o", exe] + objs)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    for seed in (1, 2, 3):
+        r = subprocess.run([exe, "20000", str(seed)], capture_output=True, text=True, timeout=300, env=env)
+        assert r.returncode == 0 and r.stdout.startswith("ok "), (r.stdout, r.stderr[-3000:])
+        calls, launches, most, items = map(int, r.stdout.split()[1:5])
+        # every call launched, some needed several launches, and the largest grids reached the limit
+        assert calls == 20000 and launches >= calls and most > 1 and items == 1 << 31
