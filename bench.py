@@ -35,6 +35,8 @@ Other modes:
                       (the command to put under rocprofv3 --pmc)
   --summarize-counters DIR[,DIR]   turn the rocprofv3 counter CSVs found in
                       the directories into profiles/counters_<workload>.json
+  --summarize-spread GLOB   counter-run logs of fresh processes (plain or
+                      under a counter pass) -> profiles/spread_<workload>.json
 """
 from __future__ import annotations
 
@@ -861,6 +863,8 @@ def main():
                     help="the pack reads per-rank KV lengths and neutralises tokens whose length is 0")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--summarize-counters", default=None)
+    ap.add_argument("--summarize-spread", default=None,
+                    help="glob of counter-run logs of fresh processes -> profiles/spread_<key>.{json,md}")
     ap.add_argument("--summarize-trace", default=None,
                     help="rocprofv3 --kernel-trace --stats output directory -> profiles/trace_<key>.{json,md}")
     args = ap.parse_args()
@@ -870,6 +874,9 @@ def main():
     B = args.B if args.B is not None or not default_run else HEADLINE[1]
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, key, B)
+        return
+    if args.summarize_spread:
+        summarize_spread(args.summarize_spread, key, B)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, key, B, command=os.environ.get("DCP_TRACE_COMMAND"),
@@ -937,10 +944,28 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def dpm_levels():
+    """Current shader and memory clock levels from the amdgpu sysfs DPM
+    tables (the entry marked '*'), for every card the process can see."""
+    out = []
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for f in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(d, f)) as fh:
+                    cur = [ln.split(":", 1)[-1].replace("*", "").strip() for ln in fh if "*" in ln]
+            except OSError:
+                continue
+            if cur:
+                out.append("%s %s" % (f[len("pp_dpm_"):], cur[0]))
+    return ", ".join(out) or "n/a"
+
+
 def counter_run(wl):
     """For rocprofv3 --pmc: a plain elementwise pass over 1 GiB (the scale
-    reference: 1 GiB read, 1 GiB written), then three launches of each kernel
-    of the workload."""
+    reference: 1 GiB read, 1 GiB written), then three calls of each kernel of
+    the workload (its first three buffer sets, or its one call three times),
+    each timed with events so that a counter pass also gives the rate of the
+    allocation it ran on."""
     import torch
 
     n = 1 << 28
@@ -951,12 +976,21 @@ def counter_run(wl):
     torch.cuda.synchronize()
     del a, b
     for name, nbytes, launches in wl.kernels():
-        for f in launches[:3]:
+        calls = (launches * 3)[:3]
+        for i, f in enumerate(calls):
             if hasattr(wl, "restore"):
                 wl.restore()
+            # the counters serialise dispatches; events on the launching
+            # stream still time this call alone
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             f()
-        torch.cuda.synchronize()
-        print("# counter run: %s x3, %d algorithmic bytes per launch" % (name, nbytes), flush=True)
+            e1.record()
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3
+            print("# counter run: %s call %d: %.1f us, %.1f GB/s (clocks after it: %s)"
+                  % (name, i, us, nbytes / us / 1e3, dpm_levels()), flush=True)
+        print("# counter run: %s x%d, %d algorithmic bytes per launch" % (name, len(calls), nbytes), flush=True)
 
 
 def counter_key(workload, B=None):
@@ -1032,6 +1066,136 @@ def summarize_counters(directory, workload, B=None):
     with open(os.path.join(ROOT, "profiles", "counters_%s.md" % key), "w") as fo:
         fo.write(counters_markdown(out, directory))
     print(json.dumps(out, indent=1))
+
+
+# counter sets of the placement study (one rocprofv3 --pmc pass each)
+SPREAD_COUNTER_SETS = {
+    "latency": "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_LEVEL_sum",
+    "stalls": "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum TCC_TAG_STALL_sum "
+              "GRBM_GUI_ACTIVE",
+    "tlb": "TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum "
+           "TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS_sum TCP_UTCL1_SERIALIZATION_STALL_sum",
+}
+
+
+def summarize_spread(pattern, workload, B=None, out_dir=None):
+    """Runs of `bench.py --counter-run` in fresh processes (each its own
+    allocation of the workload's buffers), plain or under one rocprofv3 --pmc
+    pass -> profiles/spread_<key>.{json,md}.  PATTERN globs the runs' stdout
+    logs; a counter pass keeps its rocprofv3 directory beside its log (the
+    log's path without .log).  Per process: the rate of each call it timed,
+    and per call of its kernel the counters of that pass (EA read and write
+    latency from the in-flight levels, DRAM credit and tag stalls per busy
+    cycle, L1 TLB misses)."""
+    import csv
+    import statistics
+
+    key = counter_key(workload, B)
+    fam = {"kimi": r"\binplace_kernel", "kimi-rs": r"\bcombine_(wave_)?kernel"}.get(workload, r"_kernel")
+    procs = []
+    for log in sorted(glob.glob(pattern)):
+        text = open(log).read()
+        rates = [float(m.group(1)) for m in re.finditer(r"# counter run: \S+ call \d+: [\d.]+ us, ([\d.]+) GB/s", text)]
+        clocks = re.findall(r"# counter run: \S+ call \d+: .*\(clocks after it: ([^)]*)\)", text)
+        if not rates:
+            continue
+        by = {}
+        for path in glob.glob(os.path.join(log[:-len(".log")], "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if re.search(fam, r.get("Kernel_Name", "")):
+                        name = r["Counter_Name"][:-4] if r["Counter_Name"].endswith("_sum") else r["Counter_Name"]
+                        by.setdefault(name, []).append(float(r["Counter_Value"]))
+        m = {}
+        if "TCC_EA0_RDREQ_LEVEL" in by:
+            m["ea_read_latency_cycles"] = sum(by["TCC_EA0_RDREQ_LEVEL"]) / sum(by["TCC_EA0_RDREQ"])
+        if "TCC_EA0_WRREQ_LEVEL" in by:
+            m["ea_write_latency_cycles"] = sum(by["TCC_EA0_WRREQ_LEVEL"]) / sum(by["TCC_EA0_WRREQ"])
+        if "GRBM_GUI_ACTIVE" in by:
+            busy = sum(by["GRBM_GUI_ACTIVE"])
+            for c, label in (("TCC_EA0_RDREQ_DRAM_CREDIT_STALL", "read_credit_stall_per_busy_cycle"),
+                             ("TCC_EA0_WRREQ_DRAM_CREDIT_STALL", "write_credit_stall_per_busy_cycle"),
+                             ("TCC_TAG_STALL", "tag_stall_per_busy_cycle")):
+                if c in by:
+                    m[label] = sum(by[c]) / busy
+        if "TCP_UTCL1_TRANSLATION_MISS" in by:
+            n = len(by["TCP_UTCL1_TRANSLATION_MISS"])
+            m["utcl1_misses_per_call"] = sum(by["TCP_UTCL1_TRANSLATION_MISS"]) / n
+            for c, label in (("TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS", "utcl2_credit_stalls_per_call"),
+                             ("TCP_UTCL1_SERIALIZATION_STALL", "utcl1_serialization_stalls_per_call")):
+                if c in by:
+                    m[label] = sum(by[c]) / n
+        procs.append({"run": os.path.basename(log)[:-len(".log")], "counters": bool(by),
+                      "rate_GBps": rates, "mean_GBps": sum(rates) / len(rates), "clocks": clocks, **m})
+    if not procs:
+        raise SystemExit("no counter-run logs match %s" % pattern)
+    plain = [p["mean_GBps"] for p in procs if not p["counters"]]
+    pmc = [p["mean_GBps"] for p in procs if p["counters"]]
+    target = 0.7 * PEAK_HBM_GBS
+
+    def stats(v):
+        return {"processes": len(v), "median_GBps": statistics.median(v), "min_GBps": min(v), "max_GBps": max(v),
+                "at_least_70pct": sum(x >= target for x in v)} if v else None
+
+    out = {"kernel_source": kernel_source_hash(), "workload": workload, "key": key,
+           "plain": stats(plain), "under_counters": stats(pmc), "processes": procs}
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "spread_%s.json" % key), "w") as fo:
+        json.dump(out, fo, indent=1)
+    with open(os.path.join(out_dir, "spread_%s.md" % key), "w") as fo:
+        fo.write(spread_markdown(out, pattern))
+    print(json.dumps({k: v for k, v in out.items() if k != "processes"}, indent=1))
+
+
+def spread_markdown(d, pattern):
+    w = d["workload"]
+    cols = [("ea_read_latency_cycles", "EA read latency (cycles)", "%.0f"),
+            ("ea_write_latency_cycles", "EA write latency (cycles)", "%.0f"),
+            ("read_credit_stall_per_busy_cycle", "DRAM read credit stalls / busy cycle", "%.3f"),
+            ("write_credit_stall_per_busy_cycle", "DRAM write credit stalls / busy cycle", "%.3f"),
+            ("tag_stall_per_busy_cycle", "L2 tag stalls / busy cycle", "%.3f"),
+            ("utcl1_misses_per_call", "L1 TLB misses per call", "%.0f"),
+            ("utcl2_credit_stalls_per_call", "UTCL2 credit stalls per call", "%.0f")]
+
+    def line(s, label):
+        if not s:
+            return "- %s: none" % label
+        return ("- %s: %d processes, median %.0f GB/s (%.1f%% of 8 TB/s), range %.0f-%.0f GB/s, %d of them at "
+                "70%% of peak or more" % (label, s["processes"], s["median_GBps"], s["median_GBps"] / PEAK_HBM_GBS * 100,
+                                          s["min_GBps"], s["max_GBps"], s["at_least_70pct"]))
+
+    lines = [
+        "# Rate spread over allocations: %s workload" % w,
+        "",
+        "Kernel source hash `%s` (`spread_%s.json`).  Each row is a fresh process: it" % (d["kernel_source"], d["key"]),
+        "allocates the workload's buffers, then times three calls of the kernel with",
+        "events (`bench.py --counter-run`), either plain or under one rocprofv3 counter",
+        "pass.  Commands (each run a new process, K numbering the runs):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        "python3 $REPO/bench.py --workload %s --counter-run > $REPO/gpurun_out/ea_plainK.log" % w,
+    ]
+    for name, cs in SPREAD_COUNTER_SETS.items():
+        lines.append("rocprofv3 --pmc %s --output-format csv -d $REPO/gpurun_out/ea_%sK -o run -- python3 "
+                     "$REPO/bench.py --workload %s --counter-run > $REPO/gpurun_out/ea_%sK.log" % (cs, name, w, name))
+    lines += [
+        "python3 bench.py --workload %s --summarize-spread '%s'" % (w, pattern),
+        "```",
+        "",
+        line(d["plain"], "plain"),
+        line(d["under_counters"], "under a counter pass"),
+        "",
+        "| Run | GB/s (mean of its calls) | Calls | Clocks after its last call | "
+        + " | ".join(c[1] for c in cols) + " |",
+        "|---|---|---|---|" + "---|" * len(cols),
+    ]
+    for p in sorted(d["processes"], key=lambda p: (p["counters"], p["mean_GBps"])):
+        cells = [(fmt % p[k]) if k in p else "" for k, _, fmt in cols]
+        lines.append("| %s | %.0f | %s | %s | %s |" % (p["run"], p["mean_GBps"], ", ".join("%.0f" % r for r in p["rate_GBps"]),
+                                                        (p.get("clocks") or ["n/a"])[-1], " | ".join(cells)))
+    return "\n".join(lines) + "\n"
 
 
 def counters_markdown(d, directory):

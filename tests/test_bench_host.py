@@ -102,3 +102,52 @@ def test_trace_summary_groups_launch_shapes_and_labels_them(tmp_path):
     assert t["stats"][0]["kernel"] == "pack_stream_kernel<1, 8, true, false, true>"
     assert "| `pack_stream_kernel<1, 8, true, false, true>` | 147456 x 512 |" in (out / "trace_longctx_B512.md").read_text()
     assert bench._short_kernel_name("void at::cuda::(anonymous namespace)::spin_kernel(long)") == "at::cuda::spin_kernel"
+
+
+def test_spread_summary_pairs_each_process_with_its_counters(tmp_path):
+    """--summarize-spread: each fresh process's timed calls (from its
+    counter-run log) with the counters of its kernel's launches (from the
+    rocprofv3 directory beside the log); plain logs have no counters."""
+    import csv
+    import json
+
+    kern = "void dcp::(anonymous namespace)::inplace_kernel<dcp::F32T, 16, 64, 8, 8, 1, true>(dcp::(anonymous namespace)::InplK)"
+
+    def log(name, rates):
+        (tmp_path / (name + ".log")).write_text("# generated\n" + "".join(
+            "# counter run: inplace call %d: 10000.0 us, %.1f GB/s (clocks after it: sclk 2000Mhz, mclk 2000Mhz)\n"
+            % (i, r) for i, r in enumerate(rates)) + "# counter run: inplace x3, 1 algorithmic bytes per launch\n")
+
+    def counters(name, values):
+        d = tmp_path / name
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+            for cn, vs in values.items():
+                for v in vs:
+                    w.writerow([kern, cn, v])
+                    w.writerow(["void at::native::neg_kernel()", cn, 1.0])
+
+    log("ea_plain1", [5400.0, 5500.0, 5600.0])
+    log("ea_plain2", [6000.0, 6000.0, 6000.0])
+    log("ea_latency1", [5700.0, 5700.0, 5700.0])
+    counters("ea_latency1", {"TCC_EA0_RDREQ_sum": [100.0, 100.0], "TCC_EA0_RDREQ_LEVEL_sum": [300000.0, 340000.0],
+                             "TCC_EA0_WRREQ_sum": [200.0, 200.0], "TCC_EA0_WRREQ_LEVEL_sum": [100000.0, 120000.0]})
+    log("ea_tlb1", [5300.0, 5300.0, 5300.0])
+    counters("ea_tlb1", {"TCP_UTCL1_TRANSLATION_MISS_sum": [65536.0, 65536.0],
+                         "TCP_UTCL1_STALL_UTCL2_REQ_OUT_OF_CREDITS_sum": [0.0, 0.0]})
+    out = tmp_path / "out"
+    bench.summarize_spread(str(tmp_path / "ea_*.log"), "kimi", None, out_dir=str(out))
+    d = json.load(open(out / "spread_kimi.json"))
+    by = {p["run"]: p for p in d["processes"]}
+    assert by["ea_plain1"]["mean_GBps"] == 5500.0 and not by["ea_plain1"]["counters"]
+    assert by["ea_latency1"]["ea_read_latency_cycles"] == 3200.0
+    assert by["ea_latency1"]["ea_write_latency_cycles"] == 550.0
+    assert by["ea_tlb1"]["utcl1_misses_per_call"] == 65536.0
+    assert by["ea_plain2"]["clocks"][-1] == "sclk 2000Mhz, mclk 2000Mhz"
+    assert d["plain"] == {"processes": 2, "median_GBps": 5750.0, "min_GBps": 5500.0, "max_GBps": 6000.0,
+                          "at_least_70pct": 1}
+    assert d["under_counters"]["processes"] == 2 and d["under_counters"]["at_least_70pct"] == 1
+    md = (out / "spread_kimi.md").read_text()
+    assert "| ea_latency1 | 5700 | 5700, 5700, 5700 | sclk 2000Mhz, mclk 2000Mhz | 3200 | 550 |" in md
