@@ -16,8 +16,9 @@
  *     allocates, frees, zero-fills, synchronises or copies to the host, so the
  *     calls can be captured in a HIP graph.
  *   - Work is enqueued only on `stream` (a hipStream_t passed as void*; NULL is
- *     the null stream).  Calls keep no state between them, so calls on
- *     different streams may run concurrently.
+ *     the null stream).  The stream and every pointer belong to the calling
+ *     thread's current HIP device (hipSetDevice).  Calls keep no state
+ *     between them, so calls on different streams may run concurrently.
  *   - Payload tensors hold `dtype` elements; the innermost (D) dimension is
  *     contiguous.  Every other stride is given in ELEMENTS of that tensor's
  *     own type: payload strides in payload elements, LSE strides in fp32

@@ -43,15 +43,18 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _invoke(name: str, args: tuple, timing) -> None:
+def _invoke(name: str, args: tuple, timing, device: torch.device) -> None:
     """Call `name` of libdcpmerge.so with the marshalled arguments, or its
-    timed twin of the measurement library when timing events are given."""
-    if timing is None:
-        st = getattr(_lib.lib(), name)(*args)
-    else:
-        from . import timing as _timing
+    timed twin of the measurement library when timing events are given, with
+    the tensors' device current (the library launches on the current
+    device, on that device's stream)."""
+    with torch.cuda.device(device):
+        if timing is None:
+            st = getattr(_lib.lib(), name)(*args)
+        else:
+            from . import timing as _timing
 
-        st = _timing.call_timed(name, args, *timing)
+            st = _timing.call_timed(name, args, *timing)
     _lib.check(st, name)
 
 
@@ -144,7 +147,7 @@ def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor,
         dst_o.data_ptr(), do[0], do[1], do[2], do[3],
         dst_lse.data_ptr(), dl[0], dl[1], dl[2], dl[3],
         kv_len.data_ptr() if kv_len is not None else None, kl[0], kl[1],
-        R, N, B, H, D, _dt(out), _stream(out)), timing)
+        R, N, B, H, D, _dt(out), _stream(out)), timing, out.device)
 
 
 def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on_e: bool = True,
@@ -183,7 +186,7 @@ def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on
         out.data_ptr(), oo[0], oo[1], oo[2],
         out_lse.data_ptr() if out_lse is not None else None, ol[0], ol[1], ol[2],
         R, N, B, Hpr, D, _dt(recv_o),
-        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(recv_o)), timing)
+        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(recv_o)), timing, recv_o.device)
     if not batched:
         out = out[0]
         out_lse = out_lse[0] if out_lse is not None else None
@@ -227,5 +230,5 @@ def cp_lse_combine_inplace(partial: torch.Tensor, lse: torch.Tensor, h0: int = 0
         out.data_ptr() if out is not None else None, os_[0], os_[1],
         out_lse.data_ptr() if out_lse is not None else None, ols[0], ols[1],
         N, P, rank0, T, H, D, _dt(partial),
-        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(partial)), timing)
+        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(partial)), timing, partial.device)
     return (out, out_lse) if return_lse else out
