@@ -218,27 +218,23 @@ template <> struct Cvt<BF16T, 2> {
 // 8-bit payload, OCP FP8 E4M3: sign, 4 exponent bits (bias 7), 3 mantissa
 // bits; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN;
 // there are no infinities and the largest finite magnitude is 448.
-// Decoding uses gfx950's packed conversion (two bytes of a word per
-// instruction, exact).  Encoding rounds to nearest even in integer
-// arithmetic: a merged value is a convex combination of fp8 values, so it
-// never exceeds 448 in magnitude; anything at or beyond 448 (which the merge
-// does not produce) saturates to +-448, and NaN stays NaN.
-__device__ __forceinline__ uint32_t fp8_e4m3_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t a = u & 0x7fffffffu;
-    uint32_t c;
-    if (a > 0x7f800000u) {
-        c = 0x7fu;                                   // NaN
-    } else if (a >= 0x43e00000u) {
-        c = 0x7eu;                                   // |f| >= 448: the largest finite value
-    } else if (a < 0x3c800000u) {
-        c = (uint32_t)rintf(__uint_as_float(a) * 512.0f);   // below 2^-6: m * 2^-9, m = 0..8
-    } else {
-        // normal: keep 3 mantissa bits, ties to even; a carry moves into the exponent
-        const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-        c = (r >> 20) - (120u << 3);
-    }
-    return c | ((u >> 24) & 0x80u);
+// Decoding and encoding both use gfx950's packed conversions (two values per
+// instruction).  The decode is exact.  The hardware encode rounds to nearest
+// even but turns magnitudes of 464 and beyond into NaN, so inputs at or
+// beyond 448 are first saturated to +-448; with that, the encode below equals
+// an integer round-to-nearest-even encoder with saturation on every non-NaN
+// fp32 bit pattern (all 4,278,190,082 of them compared on MI355X, in both
+// halves of the packed word).  A merged value is a convex combination of fp8
+// values and finite (the guards see to that), so the merge never reaches the
+// saturation; NaN, which it never forms either, becomes the NaN code 0xff.
+__device__ __forceinline__ float fp8_saturate(float f) {
+    return fabsf(f) >= 448.0f ? copysignf(448.0f, f) : f;   // NaN fails the test and passes through
+}
+
+// Two fp8 codes of a and b into bytes 2*hi and 2*hi + 1 of `word`.
+template <bool HI>
+__device__ __forceinline__ int fp8_e4m3_pack2(float a, float b, int word) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(fp8_saturate(a), fp8_saturate(b), word, HI);
 }
 
 // V >= 4: four elements per word, element 4k in the lowest byte of word k.
@@ -259,8 +255,8 @@ template <int V> struct Cvt<FP8T, V> {
         Vec<V> v;
 #pragma unroll
         for (int k = 0; k < V / 4; ++k)
-            v.w[k] = fp8_e4m3_rne(f[4 * k]) | (fp8_e4m3_rne(f[4 * k + 1]) << 8) |
-                     (fp8_e4m3_rne(f[4 * k + 2]) << 16) | (fp8_e4m3_rne(f[4 * k + 3]) << 24);
+            v.w[k] = (uint32_t)fp8_e4m3_pack2<true>(f[4 * k + 2], f[4 * k + 3],
+                                                    fp8_e4m3_pack2<false>(f[4 * k], f[4 * k + 1], 0));
         return v;
     }
 };
@@ -270,7 +266,7 @@ template <> struct Cvt<FP8T, 1> {
         f[0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.b, false)[0];
     }
     static __device__ __forceinline__ Vec<1> pack(const float* f) {
-        Vec<1> v; v.b = (uint8_t)fp8_e4m3_rne(f[0]); return v;
+        Vec<1> v; v.b = (uint8_t)(fp8_e4m3_pack2<false>(f[0], 0.0f, 0) & 0xff); return v;
     }
 };
 
