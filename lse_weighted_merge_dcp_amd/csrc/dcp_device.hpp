@@ -221,10 +221,10 @@ template <> struct Cvt<BF16T, 2> {
 // Decoding and encoding both use gfx950's packed conversions (two values per
 // instruction).  The decode is exact.  The hardware encode rounds to nearest
 // even but turns magnitudes of 464 and beyond into NaN, so inputs at or
-// beyond 448 are first saturated to +-448; with that, the encode below equals
-// an integer round-to-nearest-even encoder with saturation on every non-NaN
-// fp32 bit pattern (all 4,278,190,082 of them compared on MI355X, in both
-// halves of the packed word).  A merged value is a convex combination of fp8
+// beyond 448 are first saturated to +-448; with that, the encode below is
+// round-to-nearest-even with saturation on every non-NaN fp32 bit pattern
+// (tests/fp8_encode_check.hip compares all of them, in both halves of the
+// packed word, with a nearest-even reference).  A merged value is a convex combination of fp8
 // values and finite (the guards see to that), so the merge never reaches the
 // saturation; NaN, which it never forms either, becomes the NaN code 0xff.
 __device__ __forceinline__ float fp8_saturate(float f) {

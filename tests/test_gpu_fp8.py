@@ -90,3 +90,20 @@ def test_largest_value_merges_to_itself(sign):
     lse = np.random.default_rng(7).normal(0, 2, size=(N, B, Hpr)).astype(np.float32)
     got = merge(o, lse)
     assert np.array_equal(values(got), np.full(got.shape, sign * 448.0))
+
+
+def test_encoder_is_nearest_even_on_every_fp32_pattern():
+    """tests/fp8_encode_check.hip: the kernels' fp8 encoder (gfx950's packed
+    conversion behind a saturation at 448) against a table-based
+    nearest-even reference written from the format's definition, on all
+    2^32 fp32 bit patterns in both halves of the packed word; NaN must give
+    a NaN code."""
+    import os
+    import subprocess
+
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fp8_encode_check")
+    assert os.path.exists(exe), "tests/fp8_encode_check is not built: run __graft_entry__.build()"
+    say("fp8 encode check over every fp32 pattern")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.stdout, r.stderr)
+    assert "total 4294967296 patterns, 0 differ" in r.stdout, r.stdout
