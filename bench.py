@@ -2,15 +2,20 @@
 
     python bench.py [--steps K] [--warmup W] [--workload dsv3|longctx|split|tiny|kimi|kimi-rs|dsv3fp8] [--B 64]
 
-Default workload: DeepSeek-V3-shaped MLA decode -- N=8 simulated DCP ranks,
-B=64 tokens, H=128 heads (16 per rank), D=512 (kv_lora_rank), bf16 partials,
-fp32 base-2 LSE, peer-outer interleaved send buffers [N,B,16,514].  One step
-is one decode step over 61 MLA layers; each layer packs all 8 ranks' send
-buffers (one launch) and combines all 8 destinations (one launch), the
+Default run: the long-context decode sweep at B = 512 -- N=16 simulated DCP
+ranks, 512 tokens, H=128 heads (8 per rank), D=512 bf16 partials, fp32
+base-2 LSE, per-rank KV lengths uniform 0..64K (a rank with none holds the
+neutral pair), peer-outer interleaved send buffers [N,B,8,514].  One step is
+one decode step over 61 MLA layers; each layer packs all 16 ranks' send
+buffers (one launch) and combines all 16 destinations (one launch), the
 exchange between them being a zero-copy view of the stacked send buffers.
-Every layer has its own buffers (61 distinct sets, 8.6 GB), so no layer's
-inputs are cache-resident when it runs.  The step is captured once in a HIP
-graph and replayed K times; inputs are in HBM before timing starts.
+The layers rotate over distinct buffer sets (at least four, and at least
+2 GiB of them), so no
+layer's inputs are cache-resident when it runs.  The step is captured once
+in a HIP graph and replayed K times; inputs are in HBM before timing
+starts.  The DeepSeek-V3-shaped decode (N=8, B=64, H=128, D=512 bf16) and
+the Kimi-K3-shaped in-place merge are measured after it and reported under
+"secondary".
 
 Printed: one JSON line with the whole-step throughput in GB/s of algorithmic
 bytes (what the method must move: (3N+1)(D*e+4) bytes per (token, head) for
@@ -18,11 +23,15 @@ pack + combine), microseconds per layer, the roofline entry of the dominant
 kernel (its per-launch duration inside the step, from HIP events attached to
 its own dispatches in eager replays of the step; the same kernel's launches
 replayed back to back on cold buffers give `cold_achieved`) and the CPU
-oracle timed on a bounded sample, on every host thread and on one.  Beside them: the p10/p50/p90 step time, the rate of a plain
-2 GiB device-to-device copy measured in the same run (the practical ceiling),
-and for the pack + combine workloads the per-rank share (one rank's pack and
-one destination's combine at their real shapes) and the cache-resident step
-(one layer's buffers reused by every layer).
+oracle timed on a bounded sample, on every host thread and on one.  Beside
+them: the p10/p50/p90 step time, the rate of a plain 2 GiB device-to-device
+copy measured in the same run (the practical ceiling), for every kernel a
+plain copy of the same size timed cold the same way (`copy_same_bytes`: the
+rate a copy reaches at that size, fixed costs included), and for the pack +
+combine workloads the per-rank share (one rank's pack and one destination's
+combine at their real shapes, against the empty-kernel floor of their launch
+shape and a same-size copy) and the cache-resident step (one layer's
+buffers reused by every layer).
 
 Other workloads: longctx (N=16, H=128, bf16, --B 1..512), split (peer-inside
 split layout, fp16), tiny (N=2 fp32), kimi (in-place merge over 8 ranks'
@@ -31,8 +40,8 @@ flavour: each rank's head slice, no partial write-back), dsv3fp8 (the
 DeepSeek-V3 shape with an OCP FP8 E4M3 payload: rows of D + 4 bytes).
 
 Other modes:
-  --counter-run       run a 1 GiB plain copy and a few launches of each kernel
-                      (the command to put under rocprofv3 --pmc)
+  --counter-run       run a 1 GiB plain copy and three calls of each kernel,
+                      each timed (the command to put under rocprofv3 --pmc)
   --summarize-counters DIR[,DIR]   turn the rocprofv3 counter CSVs found in
                       the directories into profiles/counters_<workload>.json
   --summarize-spread GLOB   counter-run logs of fresh processes (plain or
@@ -481,6 +490,35 @@ def copy_ceiling_gbs(dev, nbytes=2 << 30, reps=10):
     return {"runtime": runtime, "library_row_copy": library, "library_row_copy_launch": [shape.blocks, shape.threads]}
 
 
+def same_bytes_copy(dev, nbytes, reps):
+    """The library's own row copy (the N = 1 identity of dcp_unpack_combine:
+    1 KB rows plus their LSE words, copied bit for bit) moving about as many
+    bytes as one launch of a kernel that moves nbytes, timed cold like the
+    kernels: one launch per buffer set, as many sets as make at least 1 GiB
+    of distinct source (at most 256), replayed in a HIP graph.  Returns
+    {"bytes", "cold_us", "GBps", "sets"}: the rate a plain copy reaches at
+    that size, fixed costs included."""
+    import torch
+
+    from lse_weighted_merge_dcp_amd import ops
+
+    rows = max(1, int(round(nbytes / 2056)))        # each row: 1 KB + 4 B read, the same written
+    moved = rows * 2056
+    sets = max(1, min(256, math.ceil((1 << 30) / (rows * 1028))))
+    bufs = []
+    for _ in range(sets):
+        src = torch.ones((1, rows, 1, 256), dtype=torch.float32, device=dev)
+        lse = torch.zeros((1, rows, 1), dtype=torch.float32, device=dev)
+        bufs.append((src, lse, torch.empty((rows, 1, 256), dtype=torch.float32, device=dev),
+                     torch.empty((rows, 1), dtype=torch.float32, device=dev)))
+    launches = [lambda b=b: ops.dcp_lse_combine(b[0], b[1], is_lse_base_on_e=True, out=b[2], out_lse=b[3])
+                for b in bufs]
+    us, _ = per_launch_us(launches, reps=reps)
+    del launches, bufs
+    torch.cuda.empty_cache()
+    return {"bytes": moved, "cold_us": round(us, 3), "GBps": round(moved / (us * 1e-6) / 1e9, 1), "sets": sets}
+
+
 def percentiles(xs):
     xs = sorted(xs)
 
@@ -763,6 +801,11 @@ def measure(wl, key, B, args, full):
         kinfo[name] = {"us_per_launch": us, "bytes_per_launch": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
                        "cold_us_per_launch": cold, "cold_GBps": nbytes / (cold * 1e-6) / 1e9,
                        "launch": [shapes[name].blocks, shapes[name].threads]}
+        # a plain copy of the same size, cold: what the kernel's pattern
+        # would reach if it were a copy, fixed costs of a launch that size
+        # included
+        kinfo[name]["copy_same_bytes"] = same_bytes_copy(wl.dev, nbytes, reps)
+        kinfo[name]["of_copy_same_bytes"] = round(kinfo[name]["cold_GBps"] / kinfo[name]["copy_same_bytes"]["GBps"], 3)
     # every kernel of a layer run cold, one after the other: no layer's
     # inputs left in the caches by the kernel before it
     cold_us = sum(v["cold_us_per_launch"] for v in kinfo.values())
@@ -803,16 +846,20 @@ def measure(wl, key, B, args, full):
                 restore()
             shp = launch_shape_of(launches[0])
             floor = empty_floor_us(shp, len(launches), reps)
+            copy = same_bytes_copy(wl.dev, nbytes, reps)
             pr[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": nbytes,
                         "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                         "launch": [shp.blocks, shp.threads], "empty_kernel_us": round(floor, 3),
                         "net_GBps": round(nbytes / (max(us - floor, 1e-3) * 1e-6) / 1e9, 1),
-                        "net_frac": round(nbytes / (max(us - floor, 1e-3) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+                        "net_frac": round(nbytes / (max(us - floor, 1e-3) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "copy_same_bytes": copy,
+                        "of_copy_same_bytes": round(nbytes / (us * 1e-6) / 1e9 / copy["GBps"], 3)}
         if hasattr(wl, "hot_launches"):
             pr["us_per_layer"] = round(sum(v["us_per_launch"] for v in pr.values()), 3)
         pr["note"] = ("one rank's / one destination's own call at its real shape, cold; empty_kernel_us is a "
                       "graph of as many launches of an empty kernel with the same launch shape, net_GBps the "
-                      "rate net of that fixed cost")
+                      "rate net of that fixed cost; copy_same_bytes the library's plain row copy of the same "
+                      "size, cold, and of_copy_same_bytes the call's rate as a fraction of that copy's")
         res["per_rank"] = pr
     if full:
         if hasattr(wl, "hot_launches"):
