@@ -106,10 +106,11 @@ def _hipcc():
 
 def test_kernel_launches_under_asan_and_ubsan(tmp_path):
     """The real launchers of pack.hip, combine.hip and inplace.hip and the C
-    ABI of api.cpp, compiled for the host only (an empty device binary stands
-    in for the gfx950 code) with ASan and UBSan, driven by
-    tests/host_launch_check.cpp: random valid calls from tiny to far beyond
-    one launch's reach, every launch checked against the grid limits."""
+    ABIs of api.cpp and bench_api.cpp, compiled for the host only (an empty
+    device binary stands in for the gfx950 code) with ASan and UBSan, driven
+    by tests/host_launch_check.cpp: random valid calls from tiny to far
+    beyond one launch's reach, every launch checked against the grid limits,
+    the timed calls' events and launch shapes against their contract."""
     clangxx = os.path.join(ROCM, "lib", "llvm", "bin", "clang++")
     if not os.path.exists(clangxx):
         pytest.skip("ROCm's clang++ is not here")
@@ -121,7 +122,7 @@ def test_kernel_launches_under_asan_and_ubsan(tmp_path):
                  "-Xarch_host", "-fno-sanitize-recover=all",
                  "-Xarch_host", "-fno-omit-frame-pointer",
                  "-Xclang", "-fcuda-include-gpubinary", "-Xclang", str(fatbin), "-c"]
-    srcs = [os.path.join(CSRC, f) for f in ("api.cpp", "pack.hip", "combine.hip", "inplace.hip")]
+    srcs = [os.path.join(CSRC, f) for f in ("api.cpp", "bench_api.cpp", "pack.hip", "combine.hip", "inplace.hip")]
     srcs.append(os.path.join(ROOT, "tests", "host_launch_check.cpp"))
     objs = []
     for src in srcs:
