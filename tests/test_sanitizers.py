@@ -104,34 +104,41 @@ def _hipcc():
     return cand
 
 
-def test_kernel_launches_under_asan_and_ubsan(tmp_path):
-    """The real launchers of pack.hip, combine.hip and inplace.hip and the C
-    ABIs of api.cpp and bench_api.cpp, compiled for the host only (an empty
-    device binary stands in for the gfx950 code) with ASan and UBSan, driven
-    by tests/host_launch_check.cpp: random valid calls from tiny to far
-    beyond one launch's reach, every launch checked against the grid limits,
-    the timed calls' events and launch shapes against their contract."""
+def _launch_check_exe(tmp_path, csrc, include, check_src, sanitize=True):
+    """Build tests/host_launch_check.cpp against the host-only compile of the
+    library sources in csrc (an empty device binary in place of the gfx950
+    code; no HIP runtime linked: the check defines the entry points the
+    launchers call)."""
     clangxx = os.path.join(ROCM, "lib", "llvm", "bin", "clang++")
     if not os.path.exists(clangxx):
         pytest.skip("ROCm's clang++ is not here")
     fatbin = tmp_path / "empty.fatbin"
     fatbin.write_bytes(b"")
-    host_only = [_hipcc(), "-x", "hip", "--cuda-host-only", "-std=c++20", "-O1", "-g", "-w",
-                 "-I" + os.path.join(ROOT, "include"),
-                 "-Xarch_host", "-fsanitize=address,undefined",
-                 "-Xarch_host", "-fno-sanitize-recover=all",
-                 "-Xarch_host", "-fno-omit-frame-pointer",
-                 "-Xclang", "-fcuda-include-gpubinary", "-Xclang", str(fatbin), "-c"]
-    srcs = [os.path.join(CSRC, f) for f in ("api.cpp", "bench_api.cpp", "pack.hip", "combine.hip", "inplace.hip")]
-    srcs.append(os.path.join(ROOT, "tests", "host_launch_check.cpp"))
+    san = (["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+            "-Xarch_host", "-fno-omit-frame-pointer"] if sanitize else [])
+    host_only = [_hipcc(), "-x", "hip", "--cuda-host-only", "-std=c++20", "-O1", "-g", "-w", "-I" + include] + san + [
+        "-Xclang", "-fcuda-include-gpubinary", "-Xclang", str(fatbin), "-c"]
+    srcs = [os.path.join(csrc, f) for f in ("api.cpp", "bench_api.cpp", "pack.hip", "combine.hip", "inplace.hip")]
+    srcs.append(check_src)
     objs = []
     for src in srcs:
         obj = str(tmp_path / (os.path.basename(src) + ".o"))
         subprocess.check_call(host_only + [src, "-o", obj])
         objs.append(obj)
     exe = str(tmp_path / "host_launch_check")
-    # no HIP runtime is linked: the check program defines the few entry points the launchers call
-    subprocess.check_call([clangxx, "-fsanitize=address,undefined", "-o", exe] + objs)
+    subprocess.check_call([clangxx] + (["-fsanitize=address,undefined"] if sanitize else []) + ["-o", exe] + objs)
+    return exe
+
+
+def test_kernel_launches_under_asan_and_ubsan(tmp_path):
+    """The real launchers of pack.hip, combine.hip and inplace.hip and the C
+    ABIs of api.cpp and bench_api.cpp, compiled for the host only with ASan
+    and UBSan, driven by tests/host_launch_check.cpp: random valid calls from
+    tiny to far beyond one launch's reach, every launch checked against the
+    grid limits, the timed calls' events and launch shapes against their
+    contract."""
+    exe = _launch_check_exe(tmp_path, CSRC, os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "host_launch_check.cpp"))
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     for seed in (1, 2, 3):
@@ -140,3 +147,32 @@ def test_kernel_launches_under_asan_and_ubsan(tmp_path):
         calls, launches, most, items = map(int, r.stdout.split()[1:5])
         # every call launched, some needed several launches, and the largest grids reached the limit
         assert calls == 20000 and launches >= calls and most > 1 and items == 1 << 31
+
+
+@pytest.mark.parametrize("path,old,new,message", [
+    # launches allowed twice the workgroups: grids past 2^23 (2^32 work-items)
+    ("dcp_launch.hpp", "kMaxBlocksPerLaunch = int64_t(1) << 23", "kMaxBlocksPerLaunch = int64_t(1) << 24",
+     "launch outside the limits"),
+    # the start event left on every launch of a call
+    ("dcp_launch.hpp", "    t->start = nullptr;\n    return e;", "    return e;",
+     "timing events or launch shape not as documented"),
+])
+def test_launch_check_rejects_planted_mistakes(tmp_path, path, old, new, message):
+    """The launcher check has teeth: a copy of the library sources with one
+    planted mistake (no sanitizers) must fail it with the matching report."""
+    import shutil
+
+    root = tmp_path / "src"
+    csrc = root / "pkg" / "csrc"
+    shutil.copytree(CSRC, csrc, ignore=shutil.ignore_patterns("_build", "__pycache__", "*.py"))
+    shutil.copytree(os.path.join(ROOT, "include"), root / "include")
+    (root / "tests").mkdir()
+    text = (csrc / path).read_text()
+    assert text.count(old) == 1, "the planted mistake no longer applies to %s" % path
+    (csrc / path).write_text(text.replace(old, new))
+    check = (root / "tests" / "host_launch_check.cpp")
+    check.write_text(open(os.path.join(ROOT, "tests", "host_launch_check.cpp")).read().replace(
+        '#include "../lse_weighted_merge_dcp_amd/csrc/dcpmerge_bench.h"', '#include "../pkg/csrc/dcpmerge_bench.h"'))
+    exe = _launch_check_exe(tmp_path, str(csrc), str(root / "include"), str(check), sanitize=False)
+    r = subprocess.run([exe, "20000", "1"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1 and message in r.stderr, (r.returncode, r.stdout, r.stderr[-2000:])
