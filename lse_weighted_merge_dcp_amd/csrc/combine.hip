@@ -264,12 +264,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 // that do not divide a destination's rows, such as 384 or 768 at B = 512,
 // were slower than either.)
 constexpr uint32_t kWaveChunk = 256;
+// Large launches of at most kWaveChunkWideMaxBlocks workgroups take chunks of
+// 512 (a template parameter, like the chunk itself): the long-context B = 512
+// combine (16,384 workgroups) 180 -> 177 us; the Kimi-K3-shaped
+// reduce-scatter merge (786,432 workgroups) keeps 256, which it prefers.
+constexpr uint32_t kWaveChunkWide = 512;
+constexpr int64_t kWaveChunkWideMaxBlocks = 65536;
 
-template <typename DT, int NT, bool HOIST, int WPB, bool NTS>
+template <typename DT, int NT, bool HOIST, int WPB, bool NTS, uint32_t CH = kWaveChunk>
 __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     using C = Cvt<DT, 16>;
     constexpr int EPV = C::n;
-    const uint32_t blk = xcd_chunk_block<kWaveChunk>();
+    const uint32_t blk = xcd_chunk_block<CH>();
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t j = lane & 15u;
@@ -408,6 +414,11 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
                 if (rows <= kHoistMaxRows)
                     e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false>, dim3((uint32_t)rows), dim3(64), stream,
                                       k, a.timing);
+                else if (rows >= kHoistMinRowsLarge && blocks <= kWaveChunkWideMaxBlocks)
+                    e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 4, true, kWaveChunkWide>,
+                                               dim3((uint32_t)blocks), dim3(256), stream, k, a.timing)
+                               : launch_kernel(combine_wave_kernel<DT, NT, true, 4, false, kWaveChunkWide>,
+                                               dim3((uint32_t)blocks), dim3(256), stream, k, a.timing);
                 else if (rows >= kHoistMinRowsLarge)
                     e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 4, true>, dim3((uint32_t)blocks),
                                                dim3(256), stream, k, a.timing)

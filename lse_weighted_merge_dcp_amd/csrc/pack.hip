@@ -170,21 +170,36 @@ constexpr int64_t kStreamNtSourceBytes = int64_t(96) << 20;
 // 95.9 -> 104.6 us; B = 64 -8%).
 constexpr int64_t kStreamNtDestBytes = int64_t(768) << 20;
 
+// Launches of at least this many workgroups run their blocks in XCD-chunked
+// order (the XCDs take turns on chunks of kStreamChunk consecutive
+// workgroups) instead of plain order.  The order is a template parameter:
+// choosing it at run time inside the kernel slowed every launch, the small
+// ones most (the fp8 decode pack 14.5 -> 16.1 us).  Measured on MI355X,
+// long-context decode, 61 layers: B = 64 (18,432 workgroups) step 6.02 ->
+// 6.37 TB/s, B = 256 6.26 -> 6.51, B = 512 6.07 -> 6.14 (with the combine's
+// wider chunks); the DeepSeek-V3 pack (8,704 workgroups) lost 5% in chunked
+// order and keeps the plain one, as do smaller launches; chunks of 256 were
+// 3% slower at B = 512.
+constexpr uint32_t kStreamChunkedBlocks = 16384;
+constexpr uint32_t kStreamChunk = 64;
+
 // TWO: rows of 512 to 1020 bytes, where a wave-step can hold a second LSE
 // word; rows of 1 KB and more keep the one-LSE form.  NTS: send blocks
 // written with the nontemporal hint (a compile-time choice: with a runtime
 // flag the compiler merges the two stores into one plain store).
-template <int U, int WPB, bool NTL, bool TWO, bool NTS>
+template <int U, int WPB, bool NTL, bool TWO, bool NTS, uint32_t CH = 0>
 __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
+    uint32_t bx = blockIdx.x;
+    if constexpr (CH != 0) bx = xcd_chunk_block<CH>();   // XCDs take turns on chunks of CH workgroups
     Vec<16> v[U];
     char* dp[U];
     bool on[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         on[u] = false;
-        const uint32_t ws = (blockIdx.x * (uint32_t)U + (uint32_t)u) * (uint32_t)WPB + wave;  // wave-uniform
+        const uint32_t ws = (bx * (uint32_t)U + (uint32_t)u) * (uint32_t)WPB + wave;  // wave-uniform
         if (ws < k.nsteps) {
             const uint32_t blk = fdiv(ws, k.f_S);       // blocks ordered (r, b, p): sequential source reads
             const uint32_t s = ws - blk * k.S;
@@ -259,16 +274,25 @@ bool stream_layout(const PackArgs& a) {
     return true;
 }
 
+template <bool TWO, uint32_t CH>
+hipError_t launch_wide(const StreamK& k, uint32_t blocks, bool nt_source, bool nt_dest, hipStream_t stream,
+                       CallTiming* t) {
+    if (nt_dest)
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, true, CH>, dim3(blocks), dim3(512), stream, k,
+                             t);
+    if (nt_source)
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, false, CH>, dim3(blocks), dim3(512), stream, k,
+                             t);
+    return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO, false, CH>, dim3(blocks), dim3(512), stream, k, t);
+}
+
 template <bool TWO>
 hipError_t launch_stream(const StreamK& k, bool nt_source, bool nt_dest, hipStream_t stream, CallTiming* t) {
     if (k.nsteps >= kStreamWide) {
         const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
-        if (nt_dest)
-            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, true>, dim3(blocks), dim3(512), stream, k, t);
-        if (nt_source)
-            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, false>, dim3(blocks), dim3(512), stream, k,
-                                 t);
-        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO, false>, dim3(blocks), dim3(512), stream, k, t);
+        if (blocks >= kStreamChunkedBlocks)
+            return launch_wide<TWO, kStreamChunk>(k, blocks, nt_source, nt_dest, stream, t);
+        return launch_wide<TWO, 0>(k, blocks, nt_source, nt_dest, stream, t);
     }
     const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
     return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO, false>, dim3(blocks), dim3(256), stream, k, t);
