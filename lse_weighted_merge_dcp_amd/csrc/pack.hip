@@ -182,7 +182,9 @@ constexpr int64_t kStreamNtDestBytes = int64_t(768) << 20;
 // 6.37 TB/s, B = 256 6.26 -> 6.51, B = 512 6.07 -> 6.14 (with the combine's
 // wider chunks); the DeepSeek-V3 pack (8,704 workgroups) lost 5% in chunked
 // order and keeps the plain one, as do smaller launches; chunks of 256 were
-// 3% slower at B = 512.
+// 3% slower at B = 512, chunks of 32 and 128 within 1% of 64 (each worse at
+// one of B = 64, 256, 512) and chunks of 72 (four whole tokens at this
+// shape) 1% slower.
 constexpr uint32_t kStreamChunkedBlocks = 16384;
 constexpr uint32_t kStreamChunk = 64;
 
