@@ -266,8 +266,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 constexpr uint32_t kWaveChunk = 256;
 // Large launches of at most kWaveChunkWideMaxBlocks workgroups take chunks of
 // 512 (a template parameter, like the chunk itself): the long-context B = 512
-// combine (16,384 workgroups) 180 -> 177 us; the Kimi-K3-shaped
-// reduce-scatter merge (786,432 workgroups) keeps 256, which it prefers.
+// combine (16,384 workgroups) 180 -> 177 us, while chunks of 1024 and 2048
+// took it to 193 and 201 us; the Kimi-K3-shaped reduce-scatter merge
+// (786,432 workgroups) keeps 256, which it prefers.
 constexpr uint32_t kWaveChunkWide = 512;
 constexpr int64_t kWaveChunkWideMaxBlocks = 65536;
 
