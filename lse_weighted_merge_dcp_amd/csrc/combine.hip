@@ -264,13 +264,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 // that do not divide a destination's rows, such as 384 or 768 at B = 512,
 // were slower than either.)
 constexpr uint32_t kWaveChunk = 256;
-// Large launches of at most kWaveChunkWideMaxBlocks workgroups take chunks of
-// 512 (a template parameter, like the chunk itself): the long-context B = 512
-// combine (16,384 workgroups) 180 -> 177 us, while chunks of 1024 and 2048
-// took it to 193 and 201 us; the Kimi-K3-shaped reduce-scatter merge
-// (786,432 workgroups) keeps 256, which it prefers.
-constexpr uint32_t kWaveChunkWide = 512;
-constexpr int64_t kWaveChunkWideMaxBlocks = 65536;
+// Large launches of at most kWaveWideMaxRows rows run in 2-wave workgroups
+// whose XCDs take turns on chunks of 1024 of them (2048 rows per chunk; a
+// template parameter, like the chunk itself).  Measured on MI355X against
+// 4-wave workgroups in chunks of 256: the long-context B = 512 combine
+// (65,536 rows) 180 -> 176 us, B = 256 (32,768 rows) 91.4 -> 88.0 us in the
+// step (its step +1.1%).  4-wave workgroups in chunks of 1024 and 2048
+// (4096 and 8192 rows per turn) took B = 512 to 193 and 201 us.  The
+// Kimi-K3-shaped reduce-scatter merge (3.1M rows) keeps 4-wave workgroups
+// in chunks of 256, which it prefers.
+constexpr uint32_t kWaveChunkWide = 1024;
+constexpr int64_t kWaveWideMaxRows = 262144;
 
 template <typename DT, int NT, bool HOIST, int WPB, bool NTS, uint32_t CH = kWaveChunk>
 __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
@@ -415,11 +419,11 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
                 if (rows <= kHoistMaxRows)
                     e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false>, dim3((uint32_t)rows), dim3(64), stream,
                                       k, a.timing);
-                else if (rows >= kHoistMinRowsLarge && blocks <= kWaveChunkWideMaxBlocks)
-                    e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 4, true, kWaveChunkWide>,
-                                               dim3((uint32_t)blocks), dim3(256), stream, k, a.timing)
-                               : launch_kernel(combine_wave_kernel<DT, NT, true, 4, false, kWaveChunkWide>,
-                                               dim3((uint32_t)blocks), dim3(256), stream, k, a.timing);
+                else if (rows >= kHoistMinRowsLarge && rows <= kWaveWideMaxRows)
+                    e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 2, true, kWaveChunkWide>,
+                                               dim3((uint32_t)((rows + 1) / 2)), dim3(128), stream, k, a.timing)
+                               : launch_kernel(combine_wave_kernel<DT, NT, true, 2, false, kWaveChunkWide>,
+                                               dim3((uint32_t)((rows + 1) / 2)), dim3(128), stream, k, a.timing);
                 else if (rows >= kHoistMinRowsLarge)
                     e = nt_out ? launch_kernel(combine_wave_kernel<DT, NT, true, 4, true>, dim3((uint32_t)blocks),
                                                dim3(256), stream, k, a.timing)
