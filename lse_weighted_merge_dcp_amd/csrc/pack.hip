@@ -147,9 +147,10 @@ struct StreamK {
 // on the DeepSeek-V3-shaped pack and up to 20% on small launches, where more
 // waves spread the same bytes over more CUs.
 constexpr int kStreamU = 1;
-// Launches of at least this many wave-steps use 8-wave workgroups, smaller
-// ones 4-wave workgroups (measured: 1.5-2% faster on large launches, 1-3%
-// slower on small ones).
+// Launches of at least this many wave-steps (and fewer than
+// kStreamChunkedSteps, below) use 8-wave workgroups, smaller ones 4-wave
+// workgroups, both in plain order (measured: 8-wave 1.5-2% faster at these
+// sizes, 1-3% slower on small launches).
 constexpr int64_t kStreamWide = 32768;
 // Calls whose source partials span at least this many bytes read them with
 // the nontemporal hint (each source line is read once).  Above it a layer's
@@ -170,23 +171,23 @@ constexpr int64_t kStreamNtSourceBytes = int64_t(96) << 20;
 // 95.9 -> 104.6 us; B = 64 -8%).
 constexpr int64_t kStreamNtDestBytes = int64_t(768) << 20;
 
-// Launches of at least this many workgroups run their blocks in XCD-chunked
-// order (the XCDs take turns on chunks of kStreamChunk consecutive
-// workgroups) instead of plain order.  Neighbouring wave-steps share the
-// source line at their boundary (the source reads are shifted by the LSE
-// words); in one XCD's L2 it is fetched once (the long-context B = 512
-// pack's HBM reads 1.12 -> 1.08 GB).  The order is a template parameter:
-// choosing it at run time inside the kernel slowed every launch, the small
-// ones most (the fp8 decode pack 14.5 -> 16.1 us).  Measured on MI355X,
-// long-context decode, 61 layers: B = 64 (18,432 workgroups) step 6.02 ->
-// 6.37 TB/s, B = 256 6.26 -> 6.51, B = 512 6.07 -> 6.14 (with the combine's
-// wider chunks); the DeepSeek-V3 pack (8,704 workgroups) lost 5% in chunked
-// order and keeps the plain one, as do smaller launches; chunks of 256 were
-// 3% slower at B = 512, chunks of 32 and 128 within 1% of 64 (each worse at
-// one of B = 64, 256, 512) and chunks of 72 (four whole tokens at this
-// shape) 1% slower.
-constexpr uint32_t kStreamChunkedBlocks = 16384;
-constexpr uint32_t kStreamChunk = 64;
+// Launches of at least this many wave-steps run in 4-wave workgroups whose
+// XCDs take turns on chunks of kStreamChunk consecutive workgroups (512
+// wave-steps a turn) instead of in plain order.  Neighbouring wave-steps
+// share the source line at their boundary (the source reads are shifted by
+// the LSE words); in one XCD's L2 it is fetched once (the long-context B =
+// 512 pack's HBM reads 1.12 -> 1.08 GB).  The order is a template
+// parameter: choosing it at run time inside the kernel slowed every launch,
+// the small ones most (the fp8 decode pack 14.5 -> 16.1 us).  Measured on
+// MI355X, long-context decode, 61 layers, against 8-wave workgroups in plain
+// order: B = 64 (147,456 wave-steps) step 6.02 -> 6.49 TB/s, B = 256 6.26 ->
+// 6.69, B = 512 6.07 -> 6.21 (with the combine's chunked orders).  8-wave
+// workgroups in chunks of 64 gave 1-2% less; chunks of 32, 72 and 128 of
+// them within 1% of that, chunks of 256 3% less.  The DeepSeek-V3 pack
+// (69,632 wave-steps) lost 2-7% in chunked order (chunks of 8 to 64) and
+// keeps the plain one, as do smaller launches.
+constexpr uint32_t kStreamChunkedSteps = 131072;
+constexpr uint32_t kStreamChunk = 128;
 
 // TWO: rows of 512 to 1020 bytes, where a wave-step can hold a second LSE
 // word; rows of 1 KB and more keep the one-LSE form.  NTS: send blocks
@@ -279,25 +280,27 @@ bool stream_layout(const PackArgs& a) {
     return true;
 }
 
-template <bool TWO, uint32_t CH>
-hipError_t launch_wide(const StreamK& k, uint32_t blocks, bool nt_source, bool nt_dest, hipStream_t stream,
-                       CallTiming* t) {
-    if (nt_dest)
-        return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, true, CH>, dim3(blocks), dim3(512), stream, k,
-                             t);
-    if (nt_source)
-        return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, false, CH>, dim3(blocks), dim3(512), stream, k,
-                             t);
-    return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO, false, CH>, dim3(blocks), dim3(512), stream, k, t);
-}
-
 template <bool TWO>
 hipError_t launch_stream(const StreamK& k, bool nt_source, bool nt_dest, hipStream_t stream, CallTiming* t) {
+    if (k.nsteps >= kStreamChunkedSteps) {
+        const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
+        if (nt_dest)
+            return launch_kernel(pack_stream_kernel<kStreamU, 4, true, TWO, true, kStreamChunk>, dim3(blocks),
+                                 dim3(256), stream, k, t);
+        if (nt_source)
+            return launch_kernel(pack_stream_kernel<kStreamU, 4, true, TWO, false, kStreamChunk>, dim3(blocks),
+                                 dim3(256), stream, k, t);
+        return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO, false, kStreamChunk>, dim3(blocks), dim3(256),
+                             stream, k, t);
+    }
     if (k.nsteps >= kStreamWide) {
         const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
-        if (blocks >= kStreamChunkedBlocks)
-            return launch_wide<TWO, kStreamChunk>(k, blocks, nt_source, nt_dest, stream, t);
-        return launch_wide<TWO, 0>(k, blocks, nt_source, nt_dest, stream, t);
+        if (nt_dest)
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, true>, dim3(blocks), dim3(512), stream, k, t);
+        if (nt_source)
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, false>, dim3(blocks), dim3(512), stream, k,
+                                 t);
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO, false>, dim3(blocks), dim3(512), stream, k, t);
     }
     const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
     return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO, false>, dim3(blocks), dim3(256), stream, k, t);
