@@ -27,6 +27,8 @@ DEV = torch.device("cuda:0")
 @pytest.mark.parametrize("dt,N,B,Hpr,D,layout", [
     ("bf16", 8, 9, 16, 512, "interleaved"),   # stream kernel, 4-wave workgroups
     ("bf16", 16, 40, 8, 512, "interleaved"),  # stream kernel, 8-wave workgroups (>= 32768 wave-steps)
+    ("bf16", 16, 64, 8, 512, "interleaved"),  # stream kernel, XCD-chunked 4-wave workgroups (>= 131072 wave-steps)
+    ("fp8", 16, 128, 8, 512, "interleaved"),  # the same launch with two LSE words per wave-step
     ("f32", 2, 7, 4, 64, "interleaved"),      # row kernel (short rows)
     ("f16", 4, 6, 16, 128, "split"),          # split layout
     ("fp8", 8, 9, 16, 512, "interleaved"),    # fp8: two-LSE stream kernel (516-byte rows)

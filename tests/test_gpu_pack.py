@@ -143,6 +143,47 @@ def test_pack_interleaved_stream_shapes(dt, N, B, Hpr, D):
     assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
 
 
+# Calls of 131,072 wave-steps and more run in 4-wave workgroups whose XCDs
+# take turns on chunks of 128; the long-context workloads above reach them
+# with nontemporal loads (and stores at B = 512).  These cases reach the same
+# launch with ragged batches, plain loads and rows of 516 bytes.
+LARGE_SHAPES = [
+    ("bf16", 16, 16, 60, 8, 512),   # nontemporal source loads, B = 4 * 15
+    ("bf16", 16, 16, 58, 8, 512),   # B = 2 * 29
+    ("bf16", 16, 16, 57, 8, 512),   # B odd
+    ("bf16", 16, 64, 64, 1, 518),   # Hpr = 1, blocks of 65 chunks, 65 MiB of source: plain loads
+    ("f32", 16, 16, 112, 8, 128),   # rows of 516 B: two LSE words in most wave-steps
+]
+
+
+@pytest.mark.parametrize("dt,R,N,B,Hpr,D", LARGE_SHAPES)
+def test_pack_large_launch_shapes(dt, R, N, B, Hpr, D):
+    """Large interleaved packs of R source ranks, byte for byte with guard
+    bands; NaN, -inf and +inf LSEs among them."""
+    say("pack large launch shapes", dt, R, N, B, Hpr, D)
+    H = N * Hpr
+    esz = np.dtype(NP_DT[dt]).itemsize
+    lpd = 4 // esz
+    g = torch.Generator().manual_seed(B * 7 + D)
+    out = synth.to_storage(torch.randn(R, B, H, D, generator=g), dt)
+    lse = np.random.default_rng(B + D).normal(5, 4, size=(R, B, H)).astype(np.float32)
+    lse[0, 0, :2] = [np.nan, -np.inf]
+    lse[R - 1, B - 1, -1] = np.inf
+    shape = (R, N, B, Hpr, D + lpd)
+    buf, host = guarded(int(np.prod(shape)) * esz, seed=B + N)
+    send = dev_view(buf, TORCH_DT[dt], shape)
+    pay, words = ops.interleaved_views(send, D)
+    ops.dcp_pack_a2a_send(to_dev(out, dt, DEV), torch.from_numpy(lse).to(DEV), pay, words)
+    hsend = host_view(host, NP_DT[dt], shape)
+    hpay, hwords = orc.interleaved_views_np(hsend, D, dt)
+    for r in range(R):
+        orc.pack(out[r], lse[r], hpay[r], hwords[r], N)
+    got = buf.cpu().numpy()
+    assert np.array_equal(got, host), "pack differs at %d bytes" % int((got != host).sum())
+    del buf, send, pay, words
+    torch.cuda.empty_cache()
+
+
 SPLIT = [("f16", 4, 256, 16, 128), ("bf16", 2, 4, 8, 128), ("bf16", 4, 1, 16, 512), ("f32", 8, 3, 2, 64),
          ("fp8", 4, 8, 16, 128)]
 
