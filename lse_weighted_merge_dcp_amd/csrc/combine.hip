@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
 }
 
 
-// Row-per-wave variant (LPR = 64, 16-byte vectors, fixed N <= 16).  The
+// Row-per-wave variant (LPR = 64, VB-byte vectors, fixed N <= 16).  The
 // row is wave-uniform, so each peer row's base address sits in scalar
 // registers and all N loads share one VGPR lane offset; the weights move to
 // scalar registers too.  That keeps the kernel at 44 VGPRs for N = 8.  The
@@ -276,9 +276,12 @@ constexpr uint32_t kWaveChunk = 256;
 constexpr uint32_t kWaveChunkWide = 1024;
 constexpr int64_t kWaveWideMaxRows = 262144;
 
-template <typename DT, int NT, bool HOIST, int WPB, bool NTS, uint32_t CH = kWaveChunk>
+// VB = 4 splits each 1 KB segment of the 16-byte form into four, for the
+// smallest launches (see kNarrowMaxRows); k.chunks and k.steps then count
+// VB-byte vectors.
+template <typename DT, int NT, bool HOIST, int WPB, bool NTS, uint32_t CH = kWaveChunk, int VB = 16>
 __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
-    using C = Cvt<DT, 16>;
+    using C = Cvt<DT, VB>;
     constexpr int EPV = C::n;
     const uint32_t blk = xcd_chunk_block<CH>();
     const uint32_t wave = wave_id();
@@ -306,14 +309,14 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     const bool on = c < k.chunks;
     // lanes past the row end read its last chunk again (never stored), so
     // the loads need no branch and the LSE wait never covers them
-    const uint32_t voff = (on ? c : k.chunks - 1u) * 16u;
-    Vec<16> x[NT];
+    const uint32_t voff = (on ? c : k.chunks - 1u) * (uint32_t)VB;
+    Vec<VB> x[NT];
 
     float lj = -INFINITY;
     if (j < (uint32_t)NT) lj = load_f32(lbase + (int64_t)j * k.rl_N);
     if constexpr (HOIST) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) x[i] = gload16<true>(wave_addr(rbase + i * k.r_N), voff);
+        for (int i = 0; i < NT; ++i) x[i] = gloadv<VB, true>(wave_addr(rbase + i * k.r_N), voff);
     }
     LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj));
     float w = 0.0f;
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     }(std::make_integer_sequence<int, NT>{});
     if constexpr (!HOIST) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) x[i] = gload16<true>(wave_addr(rbase + i * k.r_N), voff);
+        for (int i = 0; i < NT; ++i) x[i] = gloadv<VB, true>(wave_addr(rbase + i * k.r_N), voff);
     }
 
     float acc[EPV];
@@ -354,12 +357,12 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             float f[EPV];
-            C::unpack(gload16<false>(wave_addr(rbase + i * k.r_N), voff), f);
+            C::unpack(gloadv<VB, false>(wave_addr(rbase + i * k.r_N), voff), f);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
         }
     }
-    if (on) vstore_out<16, NTS>(obase + voff, C::pack(acc));
+    if (on) vstore_out<VB, NTS>(obase + voff, C::pack(acc));
     if (k.olse != nullptr && lane == 0 && seg == 0)
         *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
 }
@@ -374,6 +377,17 @@ constexpr int64_t kHoistMaxRows = 2048;
 // DeepSeek-V3-shaped combine, 8192 tasks, 11.9 -> 13.3 us in HOIST order,
 // hence the gap).
 constexpr int64_t kHoistMinRowsLarge = 32768;
+// Launches of at most this many 1 KB row segments run in 4-byte vectors
+// (VB = 4): four waves per segment, each converting and summing a quarter
+// of the elements.  With so few waves on the chip, a wave's own arithmetic
+// (16 peers x 8 elements per lane in the 16-byte form) is not hidden behind
+// other waves.  Measured on MI355X, long-context decode (N = 16, D = 512
+// bf16), two paired runs: one destination's combine at B = 1 (8 rows) 3.05
+// -> 2.70 us, at B = 8 (64 rows) 3.40 -> 3.10 us, the B = 1 layer's
+// combine (128 rows) 3.59 -> 3.53 us cold; at 512 rows (B = 64) equal, at
+// 1024 (one destination at the DeepSeek-V3 shape) 4.20 -> 4.53 us, and at
+// 8-byte vectors nothing gained anywhere.
+constexpr int64_t kNarrowMaxRows = 128;
 
 template <typename DT, int V, int LPR, int NT>
 hipError_t run(const CombineArgs& a, hipStream_t stream) {
@@ -416,7 +430,17 @@ hipError_t run(const CombineArgs& a, hipStream_t stream) {
             const int64_t blocks = (rows + RPB - 1) / RPB;
             hipError_t e;
             if constexpr (V == 16 && LPR == 64 && NT > 0) {
-                if (rows <= kHoistMaxRows)
+                if (rows <= kNarrowMaxRows) {
+                    // the same tasks in 4-byte vectors: segments of 256 bytes
+                    const int64_t ch4 = a.D * DT::esize / 4;
+                    const int64_t st4 = (ch4 + 63) / 64;
+                    k.chunks = (uint32_t)ch4;
+                    k.steps = (uint32_t)st4;
+                    k.rows = (uint32_t)(nr * nb * a.Hpr * st4);
+                    k.f_steps = make_fastdiv(k.steps);
+                    e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false, kWaveChunk, 4>, dim3(k.rows), dim3(64),
+                                      stream, k, a.timing);
+                } else if (rows <= kHoistMaxRows)
                     e = launch_kernel(combine_wave_kernel<DT, NT, true, 1, false>, dim3((uint32_t)rows), dim3(64), stream,
                                       k, a.timing);
                 else if (rows >= kHoistMinRowsLarge && rows <= kWaveWideMaxRows)

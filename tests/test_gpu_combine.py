@@ -161,12 +161,14 @@ def test_general_shapes(dt, N, D):
 
 @pytest.mark.parametrize("dt,N,D", [("bf16", 8, 400), ("f16", 16, 384), ("f32", 4, 1000), ("bf16", 2, 512),
                                     ("fp8", 8, 1024), ("fp8", 16, 800)])
-@pytest.mark.parametrize("B", [5, 300])
+@pytest.mark.parametrize("B", [5, 40, 300])
 def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
-    """Rows of 768 bytes and more take the row-per-wave kernel: at B = 5 in
-    the latency order (payload loads issued before the LSE reduction), at
-    B = 300 (2400 rows or more) in the bandwidth order.  Rows that are not a
-    multiple of 64 16-byte chunks leave idle lanes in their last segment;
+    """Rows of 768 bytes and more take the row-per-wave kernel: at B = 5 (40
+    to 80 row segments) in the latency order (payload loads issued before
+    the LSE reduction) in 4-byte vectors, at B = 40 (320 to 640) in the same
+    order in 16-byte vectors, at B = 300 (2400 or more) in the bandwidth
+    order.  Rows that are not a multiple of 64 vectors leave idle lanes in
+    their last segment;
     NaN and +-inf planted in the payload force the guarded re-read; special
     LSE values and an all-neutral row are mixed in."""
     say("row-per-wave", dt, N, D, B)
