@@ -317,6 +317,12 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     if constexpr (HOIST) {
 #pragma unroll
         for (int i = 0; i < NT; ++i) x[i] = gloadv<VB, true>(wave_addr(rbase + i * k.r_N), voff);
+        // keep the loads here: left free, the scheduler sank the 16 loads of
+        // the 4-byte form below the wait for the LSE word (one destination's
+        // long-context combine at B = 8 3.08 -> 2.96 us); the 16-byte form
+        // keeps its own schedule, which the barrier made slower on the
+        // largest launches
+        if constexpr (VB != 16) __builtin_amdgcn_sched_barrier(0);
     }
     LseState st = reduce_lse(__builtin_isnan(lj) ? -INFINITY : lj, lse_flags(lj));
     float w = 0.0f;
