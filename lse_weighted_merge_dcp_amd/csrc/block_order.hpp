@@ -35,4 +35,16 @@ DCP_HD uint32_t xcd_chunked_order(uint32_t b, uint32_t n) {
     return full + xcd_contiguous_order(b - full, n - full);
 }
 
+// The same order computed without a branch on the grid size (both sides
+// evaluated, then selected), so that a kernel can issue all its argument
+// loads before its first wait.
+template <uint32_t C>
+DCP_HD uint32_t xcd_chunked_order_sel(uint32_t b, uint32_t n) {
+    const uint32_t full = n / (8u * C) * (8u * C);
+    const uint32_t x = b & 7u, k = b >> 3;
+    const uint32_t in_round = ((k / C) * 8u + x) * C + (k % C);
+    const uint32_t tail = full + xcd_contiguous_order(b >= full ? b - full : 0u, n - full);
+    return b < full ? in_round : tail;
+}
+
 }  // namespace dcp

@@ -98,11 +98,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
     const uint32_t li = lane % LPR;
     const uint32_t g = lane / LPR;
     const uint32_t j = lane & 15u;
-    const uint32_t task = (blk * 4u + wave) * RPW + g;
-    if (task >= k.rows) return;  // whole row groups (and so whole DPP rows) leave together
+    const uint32_t task1 = (blk * 4u + wave) * RPW + g;
+    // A row group past the end (whole DPP rows) redoes the last task and
+    // stores nothing: with no early exit, every argument load goes out before
+    // the first wait (one round trip instead of four ahead of the first
+    // load; measured on MI355X: the split workload's combine 6.60 -> 6.36 us
+    // cold, one destination's 3.60 -> 3.42 us).
+    const bool valid = task1 < k.rows;
+    const uint32_t task = valid ? task1 : k.rows - 1u;
     const bool base2 = k.base2 != 0;
 
-    const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
+    const uint32_t row = fdiv(task, k.f_steps);
     const uint32_t seg = task - row * k.steps;
     const uint32_t bb = fdiv(row, k.f_Hpr);
     const uint32_t hl = row - bb * k.Hpr;
@@ -162,8 +168,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
                 for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
             }
         }
-        if (on) vstore<V>(obase + coff, C::pack(acc));
-        if (k.olse != nullptr && li == 0 && seg == 0)
+        if (on && valid) vstore<V>(obase + coff, C::pack(acc));
+        if (k.olse != nullptr && li == 0 && seg == 0 && valid)
             *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
     } else {
         // ---- any N: lane j of every DPP row covers peers j, j+16, ... -----
@@ -228,10 +234,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombK k) {
                         for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wt, guard_f(f[e]), acc[e]);
                     }
                 }
-                vstore<V>(obase + coff, C::pack(acc));
+                if (valid) vstore<V>(obase + coff, C::pack(acc));
             }
         }
-        if (k.olse != nullptr && li == 0 && seg == 0)
+        if (k.olse != nullptr && li == 0 && seg == 0 && valid)
             *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
     }
 }
@@ -283,19 +289,31 @@ template <typename DT, int NT, bool HOIST, int WPB, bool NTS, uint32_t CH = kWav
 __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
     using C = Cvt<DT, VB>;
     constexpr int EPV = C::n;
-    const uint32_t blk = xcd_chunk_block<CH>();
+    // HOIST launches fetch every argument before their first wait: no branch
+    // on the grid size (the selecting form of the block order) or on the row
+    // count (a wave past the end redoes task 0 and stores nothing).  Measured
+    // on MI355X, two paired runs: one destination's long-context combine at
+    // B = 8 2.92 -> 2.76 us, at B = 64 4.62 -> 4.10 us, the B = 8 layer's
+    // combine 6.05 -> 5.54 us cold.  The middle range (loads after the
+    // weights) keeps the early exit: without it the DeepSeek-V3-shaped
+    // combine inside the step went 12.9 -> 13.3 us, its waves' first loads
+    // no longer staggered by the argument round trips.
+    const uint32_t blk = HOIST ? xcd_chunk_block_sel<CH>() : xcd_chunk_block<CH>();
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t j = lane & 15u;
-    const uint32_t task0 = blk * (uint32_t)WPB + wave;
-    if (task0 >= k.rows) return;  // wave-uniform
+    const uint32_t task1 = blk * (uint32_t)WPB + wave;
+    if constexpr (!HOIST)
+        if (task1 >= k.rows) return;  // wave-uniform
+    const bool valid = task1 < k.rows;   // wave-uniform
+    const uint32_t task0 = valid ? task1 : k.rows - 1u;
     // Rows run last to first: the combine that follows a pack then starts on
     // the rows whose sends the pack wrote last (measured on MI355X: the
     // DeepSeek-V3-shaped decode step 6.01 -> 6.06 TB/s, its combine 12.1 ->
     // 11.9 us inside the step; cold launches unchanged).
     const uint32_t task = k.rows - 1u - task0;
     const bool base2 = k.base2 != 0;
-    const uint32_t row = k.steps == 1 ? task : fdiv(task, k.f_steps);
+    const uint32_t row = HOIST ? fdiv(task, k.f_steps) : (k.steps == 1 ? task : fdiv(task, k.f_steps));
     const uint32_t seg = task - row * k.steps;
     const uint32_t bb = fdiv(row, k.f_Hpr);
     const uint32_t hl = row - bb * k.Hpr;
@@ -368,8 +386,8 @@ __global__ __launch_bounds__(64 * WPB) void combine_wave_kernel(const CombK k) {
             for (int e = 0; e < EPV; ++e) acc[e] = fmaf(wi[i], guard_f(f[e]), acc[e]);
         }
     }
-    if (on) vstore_out<VB, NTS>(obase + voff, C::pack(acc));
-    if (k.olse != nullptr && lane == 0 && seg == 0)
+    if (on && valid) vstore_out<VB, NTS>(obase + voff, C::pack(acc));
+    if (k.olse != nullptr && lane == 0 && seg == 0 && valid)
         *reinterpret_cast<float*>(k.olse + r * k.ol_R + b * k.ol_B + hl * k.ol_H) = st.G;
 }
 

@@ -351,6 +351,9 @@ __device__ __forceinline__ uint32_t xcd_block() { return xcd_contiguous_order(bl
 // The same with the XCDs taking turns on chunks of C blocks (block_order.hpp).
 template <uint32_t C>
 __device__ __forceinline__ uint32_t xcd_chunk_block() { return xcd_chunked_order<C>(blockIdx.x, gridDim.x); }
+// ... and computed without a branch on the grid size.
+template <uint32_t C>
+__device__ __forceinline__ uint32_t xcd_chunk_block_sel() { return xcd_chunked_order_sel<C>(blockIdx.x, gridDim.x); }
 
 __device__ __forceinline__ uint32_t wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -68,9 +68,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
         pl[u] = false;
         kvp[u] = nullptr;
         const uint32_t vrow = (blk * (uint32_t)U + (uint32_t)u) * (4u * RPW) + wave * RPW + g;
-        if (vrow < k.vrows) {
-            const uint32_t row = (k.steps == 1) ? vrow : fdiv(vrow, k.f_steps);
-            const uint32_t step = vrow - row * k.steps;
+        // With several rows per wave, a row group past the end redoes the
+        // last row and stores nothing, so no branch stands between the
+        // argument loads and the payload loads (measured on MI355X: the split
+        // workload's layer 16.3 -> 15.9 us with the same change in the
+        // combine).  One-row waves, the smallest launches, keep the early
+        // exit, which measured faster there (2-4 workgroups: 1.86 against
+        // 1.94 us).
+        const bool valid = vrow < k.vrows;
+        if (U > 1 || valid) {
+            const uint32_t vr = valid ? vrow : k.vrows - 1u;
+            const uint32_t row = U > 1 ? fdiv(vr, k.f_steps) : ((k.steps == 1) ? vr : fdiv(vr, k.f_steps));
+            const uint32_t step = vr - row * k.steps;
             const uint32_t rb = fdiv(row, k.f_H);
             const uint32_t h = row - rb * k.H;
             const uint32_t r = fdiv(rb, k.f_B);
@@ -78,13 +87,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
             const uint32_t p = fdiv(h, k.f_Hpr);
             const uint32_t hl = h - p * k.Hpr;
             const uint32_t c = step * LPR + li;
-            if (k.kv != nullptr) kvp[u] = k.kv + r * k.kv_R + b * k.kv_B;
+            if (k.kv != nullptr && valid) kvp[u] = k.kv + r * k.kv_R + b * k.kv_B;
             if (k.dst != nullptr && c < k.chunks) {
                 v[u] = vload<V>(k.src + r * k.s_R + b * k.s_B + h * k.s_H + (int64_t)c * V);
                 dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + hl * k.d_H + (int64_t)c * V;
-                pl[u] = true;
+                pl[u] = valid;
             }
-            if (k.dst_lse != nullptr && step == 0 && li == (uint32_t)u) {
+            if (k.dst_lse != nullptr && valid && step == 0 && li == (uint32_t)u) {
                 lsrc = k.src_lse + r * k.sl_R + b * k.sl_B + h * k.sl_H;
                 lrow = u;
                 ldst = k.dst_lse + r * k.dl_R + p * k.dl_N + b * k.dl_B + hl * k.dl_H;
@@ -122,9 +131,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const PackK k) {
 // payload dword j of the block comes from source dword j - k, where k is the
 // row it sits in; a chunk that holds the LSE word of row k takes three
 // payload dwords from source dwords base-1..base+2 and the LSE in between.
-// A wave-step covers 64 chunks (256 dwords); with W >= 512 bytes it holds at
-// most two LSE words (rows k and k + 1), at wave-uniform positions, so the
-// LSEs arrive through scalar loads.
+// A wave-step covers 64 chunks (256 dwords).  The lane whose chunk holds
+// row k's LSE word loads that word itself, right after its payload load.
 // ---------------------------------------------------------------------------
 struct StreamK {
     const char* src;
@@ -189,76 +197,76 @@ constexpr int64_t kStreamNtDestBytes = int64_t(768) << 20;
 constexpr uint32_t kStreamChunkedSteps = 131072;
 constexpr uint32_t kStreamChunk = 128;
 
-// TWO: rows of 512 to 1020 bytes, where a wave-step can hold a second LSE
-// word; rows of 1 KB and more keep the one-LSE form.  NTS: send blocks
-// written with the nontemporal hint (a compile-time choice: with a runtime
-// flag the compiler merges the two stores into one plain store).
-template <int U, int WPB, bool NTL, bool TWO, bool NTS, uint32_t CH = 0>
+// NTS: send blocks written with the nontemporal hint (a compile-time choice:
+// with a runtime flag the compiler merges the two stores into one plain
+// store).
+//
+// No branch stands between the argument loads and the payload load (a wave
+// past the end redoes the last wave-step and stores nothing, lanes past a
+// block redo its last chunk; the XCD order is computed without a branch),
+// and the LSE words are vector loads: scalar loads of data would share the
+// out-of-order scalar counter with the argument loads, and a wait on either
+// would wait on both.  The argument loads then take one round trip instead of
+// two or three before the payload load goes out, which is most of a small
+// launch (measured on MI355X, two paired runs: one rank's long-context pack
+// at B = 8 2.57 -> 2.31 us, at B = 1 1.96 -> 1.84 us, the DeepSeek-V3 pack
+// 24.6 -> 23.8 us cold, the fp8 decode pack 14.5 -> 13.8 us).
+template <int U, int WPB, bool NTL, bool NTS, uint32_t CH = 0>
 __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
     uint32_t bx = blockIdx.x;
-    if constexpr (CH != 0) bx = xcd_chunk_block<CH>();   // XCDs take turns on chunks of CH workgroups
+    if constexpr (CH != 0) bx = xcd_chunk_block_sel<CH>();   // XCDs take turns on chunks of CH workgroups
     Vec<16> v[U];
     char* dp[U];
     bool on[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        on[u] = false;
-        const uint32_t ws = (bx * (uint32_t)U + (uint32_t)u) * (uint32_t)WPB + wave;  // wave-uniform
-        if (ws < k.nsteps) {
-            const uint32_t blk = fdiv(ws, k.f_S);       // blocks ordered (r, b, p): sequential source reads
-            const uint32_t s = ws - blk * k.S;
-            const uint32_t rb = fdiv(blk, k.f_N);
-            const uint32_t p = blk - rb * k.N;
-            const uint32_t r = fdiv(rb, k.f_B);
-            const uint32_t b = rb - r * k.B;
-            // the LSE words in dwords [256 s, 256 s + 256) of the block: the
-            // first LSE at or after dword d0 belongs to row kl = d0 / Wd (at
-            // dword jl >= d0), the next one, Wd dwords later, to row kl + 1
-            const uint32_t d0 = s * 256u;
-            const uint32_t kl = fdiv(d0, k.f_Wd);
-            const uint32_t jl = kl * k.Wd + k.Wd - 1u;
-            const char* lrow = k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + kl) * k.sl_H;
-            uint32_t lval = kNegInfBits, lval1 = kNegInfBits;
-            if (kl < k.Hpr && jl >= d0 && jl < d0 + 256u) lval = load_word(lrow);
-            if constexpr (TWO)
-                if (kl + 1u < k.Hpr && jl + k.Wd < d0 + 256u) lval1 = load_word(lrow + k.sl_H);
-            const uint32_t q = s * 64u + lane;
-            if (q < k.Q) {
-                const uint32_t j0 = q * 4u;                   // first dword of the chunk
-                const uint32_t row = fdiv(j0, k.f_Wd);
-                const uint32_t t = k.Wd - 1u - (j0 - row * k.Wd);   // LSE position in the chunk if < 4
-                const bool has_lse = t < 4u;
-                const uint32_t base = j0 - row;               // source dword of the chunk's first payload dword
-                const char* sblk = k.src + r * k.s_R + b * k.s_B + (int64_t)(p * k.Hpr) * ((int64_t)(k.Wd - 1u) * 4);
-                const char* sp = sblk + (int64_t)(has_lse ? base - 1u : base) * 4;
-                Vec<16> x = NTL ? vload_stream<16>(sp) : vload<16>(sp);
-                // A token this rank owns no KV for is sent as the neutral pair.
-                // Its KV length is read after the payload load has gone out, so
-                // the two are in flight together and the block's rows are read
-                // (in bounds) and dropped; waiting for the length first cost the
-                // DeepSeek-V3-shaped pack 6% (22.2 -> 23.6 us).
-                if (k.kv != nullptr) {
-                    const int kvl = __builtin_nontemporal_load(reinterpret_cast<const int*>(k.kv + r * k.kv_R + b * k.kv_B));
-                    if (kvl == 0) {
-                        x = vzero<16>();
-                        lval = lval1 = kNegInfBits;
-                    }
-                }
-                if (has_lse) {
-                    uint32_t o[4];
-#pragma unroll
-                    for (int d = 0; d < 4; ++d)
-                        o[d] = (uint32_t)d < t ? x.w[d + 1] : ((uint32_t)d == t ? (TWO && row != kl ? lval1 : lval) : x.w[d]);
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) x.w[d] = o[d];
-                }
-                v[u] = x;
-                dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + (int64_t)q * 16;
-                on[u] = true;
+        const uint32_t ws1 = (bx * (uint32_t)U + (uint32_t)u) * (uint32_t)WPB + wave;  // wave-uniform
+        const bool valid = ws1 < k.nsteps;
+        const uint32_t ws = valid ? ws1 : k.nsteps - 1u;
+        const uint32_t blk = fdiv(ws, k.f_S);       // blocks ordered (r, b, p): sequential source reads
+        const uint32_t s = ws - blk * k.S;
+        const uint32_t rb = fdiv(blk, k.f_N);
+        const uint32_t p = blk - rb * k.N;
+        const uint32_t r = fdiv(rb, k.f_B);
+        const uint32_t b = rb - r * k.B;
+        const uint32_t q1 = s * 64u + lane;
+        const bool inq = q1 < k.Q;
+        const uint32_t q = inq ? q1 : k.Q - 1u;
+        const uint32_t j0 = q * 4u;                   // first dword of the chunk
+        const uint32_t row = fdiv(j0, k.f_Wd);
+        const uint32_t t = k.Wd - 1u - (j0 - row * k.Wd);   // LSE position in the chunk if < 4
+        const bool has_lse = t < 4u;
+        const uint32_t base = j0 - row;               // source dword of the chunk's first payload dword
+        const char* sblk = k.src + r * k.s_R + b * k.s_B + (int64_t)(p * k.Hpr) * ((int64_t)(k.Wd - 1u) * 4);
+        const char* sp = sblk + (int64_t)(has_lse ? base - 1u : base) * 4;
+        Vec<16> x = NTL ? vload_stream<16>(sp) : vload<16>(sp);
+        uint32_t lw = kNegInfBits;
+        if (has_lse) lw = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + row) * k.sl_H);
+        // A token this rank owns no KV for is sent as the neutral pair.  Its
+        // KV length is read after the payload load has gone out, so the two
+        // are in flight together and the block's rows are read (in bounds)
+        // and dropped; waiting for the length first cost the
+        // DeepSeek-V3-shaped pack 6% (22.2 -> 23.6 us).
+        if (k.kv != nullptr) {
+            const int kvl = __builtin_nontemporal_load(reinterpret_cast<const int*>(k.kv + r * k.kv_R + b * k.kv_B));
+            if (kvl == 0) {
+                x = vzero<16>();
+                lw = kNegInfBits;
             }
         }
+        if (has_lse) {
+            uint32_t o[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                o[d] = (uint32_t)d < t ? x.w[d + 1] : ((uint32_t)d == t ? lw : x.w[d]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) x.w[d] = o[d];
+        }
+        v[u] = x;
+        dp[u] = k.dst + r * k.d_R + p * k.d_N + b * k.d_B + (int64_t)q * 16;
+        on[u] = valid && inq;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -280,30 +288,29 @@ bool stream_layout(const PackArgs& a) {
     return true;
 }
 
-template <bool TWO>
 hipError_t launch_stream(const StreamK& k, bool nt_source, bool nt_dest, hipStream_t stream, CallTiming* t) {
     if (k.nsteps >= kStreamChunkedSteps) {
         const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
         if (nt_dest)
-            return launch_kernel(pack_stream_kernel<kStreamU, 4, true, TWO, true, kStreamChunk>, dim3(blocks),
+            return launch_kernel(pack_stream_kernel<kStreamU, 4, true, true, kStreamChunk>, dim3(blocks),
                                  dim3(256), stream, k, t);
         if (nt_source)
-            return launch_kernel(pack_stream_kernel<kStreamU, 4, true, TWO, false, kStreamChunk>, dim3(blocks),
+            return launch_kernel(pack_stream_kernel<kStreamU, 4, true, false, kStreamChunk>, dim3(blocks),
                                  dim3(256), stream, k, t);
-        return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO, false, kStreamChunk>, dim3(blocks), dim3(256),
+        return launch_kernel(pack_stream_kernel<kStreamU, 4, false, false, kStreamChunk>, dim3(blocks), dim3(256),
                              stream, k, t);
     }
     if (k.nsteps >= kStreamWide) {
         const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
         if (nt_dest)
-            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, true>, dim3(blocks), dim3(512), stream, k, t);
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, true>, dim3(blocks), dim3(512), stream, k, t);
         if (nt_source)
-            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, TWO, false>, dim3(blocks), dim3(512), stream, k,
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, true, false>, dim3(blocks), dim3(512), stream, k,
                                  t);
-        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, TWO, false>, dim3(blocks), dim3(512), stream, k, t);
+        return launch_kernel(pack_stream_kernel<kStreamU, 8, false, false>, dim3(blocks), dim3(512), stream, k, t);
     }
     const uint32_t blocks = (k.nsteps + 4 * kStreamU - 1) / (4 * kStreamU);
-    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, TWO, false>, dim3(blocks), dim3(256), stream, k, t);
+    return launch_kernel(pack_stream_kernel<kStreamU, 4, false, false>, dim3(blocks), dim3(256), stream, k, t);
 }
 
 hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
@@ -345,8 +352,7 @@ hipError_t run_stream(const PackArgs& a, hipStream_t stream) {
             k.f_N = make_fastdiv(k.N);
             k.f_B = make_fastdiv(k.B);
             k.f_Wd = make_fastdiv(k.Wd);
-            const hipError_t e = k.Wd < 256 ? launch_stream<true>(k, nt_source, nt_dest, stream, a.timing)
-                                             : launch_stream<false>(k, nt_source, nt_dest, stream, a.timing);
+            const hipError_t e = launch_stream(k, nt_source, nt_dest, stream, a.timing);
             if (e != hipSuccess) return e;
         }
     }

@@ -293,6 +293,8 @@ long check(uint32_t n) {
     for (uint32_t b = 0; b < n; ++b) {
         const uint32_t l = dcp::xcd_chunked_order<C>(b, n);
         if (l >= n || seen[l]) ++bad; else seen[l] = 1;
+        // the selecting form is the same map
+        bad += dcp::xcd_chunked_order_sel<C>(b, n) != l;
     }
     // a grid of at most 8 C blocks keeps the contiguous order
     if (n <= 8 * C)
@@ -312,7 +314,8 @@ int main() {
             // consecutive workgroups of one XCD take consecutive blocks
             if (b >= 8 && l != dcp::xcd_contiguous_order(b - 8, n) + 1) ++bad;
         }
-        bad += check<1>(n) + check<3>(n) + check<64>(n) + check<256>(n) + check<512>(n);
+        bad += check<1>(n) + check<3>(n) + check<64>(n) + check<128>(n) + check<256>(n) + check<512>(n) +
+               check<1024>(n);
     }
     // inside whole rounds, XCD x's k-th workgroup is block k mod C of chunk (k / C) * 8 + x
     for (uint32_t b = 0; b < 16384; ++b) {
@@ -328,7 +331,8 @@ int main() {
 def test_block_orders_are_bijections(tmp_path):
     """The XCD-aware workgroup orders (csrc/block_order.hpp, the same code the
     kernels run) map every grid of up to 5000 blocks, and larger ones of the
-    workloads' sizes, one to one onto its blocks."""
+    workloads' sizes, one to one onto its blocks; the branch-free form of the
+    chunked order is the same map."""
     src = tmp_path / "bo.cpp"
     src.write_text(BLOCK_ORDER_TEST)
     exe = str(tmp_path / "bo")
