@@ -25,7 +25,7 @@ DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
     ("f32", 2, 4, 8, 64, False),       # row pack, short-row combine
     ("bf16", 8, 3, 32, 512, True),     # flat-stream pack, row-per-wave combine
     ("f16", 4, 5, 12, 128, False),     # row pack, short-row combine, 3 heads per rank
-    ("fp8", 8, 3, 32, 512, True),      # fp8: two-LSE stream pack, one-row-per-wave combine
+    ("fp8", 8, 3, 32, 512, True),      # fp8: stream pack (two LSE words in most wave-steps), one-row-per-wave combine
 ])
 def test_c_client_pack_and_combine(tmp_path, dt, N, B, H, D, base2):
     assert os.path.exists(CLIENT), "tests/c_abi_client is not built: run __graft_entry__.build()"

@@ -190,20 +190,23 @@ def test_row_per_wave_kernel_guards_and_ragged_rows(dt, N, D, B):
     check_lse(gg.cpu().numpy(), gr)
 
 
-@pytest.mark.parametrize("dt,N,D,B", [
-    ("bf16", 8, 512, 4096),     # 32768 rows, 32 MiB of output: payload loads first, plain stores
-    ("bf16", 8, 512, 8192),     # 65536 rows, 64 MiB: payload loads first, nontemporal stores
-    ("f32", 2, 1000, 1100),     # 35200 row segments (4 per row), 34 MiB
-    ("fp8", 4, 1024, 8192),     # 65536 rows of 1 KB fp8, 64 MiB
+@pytest.mark.parametrize("dt,N,D,B,Hpr", [
+    ("bf16", 8, 512, 4096, 8),     # 32768 rows, 32 MiB of output: payload loads first, plain stores
+    ("bf16", 8, 512, 8192, 8),     # 65536 rows, 64 MiB: payload loads first, nontemporal stores
+    ("f32", 2, 1000, 1100, 8),     # 35200 row segments (4 per row), 34 MiB
+    ("fp8", 4, 1024, 8192, 8),     # 65536 rows of 1 KB fp8, 64 MiB
+    ("bf16", 16, 512, 10923, 3),   # 32769 rows: the last 2-wave workgroup's second wave is past the end
 ])
-def test_row_per_wave_kernel_guards_large_launches(dt, N, D, B):
+def test_row_per_wave_kernel_guards_large_launches(dt, N, D, B, Hpr):
     """Launches of 32768 row segments and more issue the payload loads before
     the LSE reduction, and merged outputs of 64 MiB and more go out with
     nontemporal stores: NaN and +-inf planted in the payload force the
     guarded re-read there too, with special LSE values and all-neutral rows;
-    every output element and every G is compared."""
-    say("row-per-wave large launch", dt, N, D, B)
-    Hpr = 8
+    every output element and every G is compared.  A wave past the last row
+    segment redoes the first one and must store nothing: out and G are
+    written into buffers with random guard bands around them, which must
+    come back unchanged."""
+    say("row-per-wave large launch", dt, N, D, B, Hpr)
     g = torch.Generator().manual_seed(N * 7 + D + B)
     o = synth.to_storage(torch.randn(N, B, Hpr, D, generator=g), dt)
     rng = np.random.default_rng(N + D + B)
@@ -215,10 +218,24 @@ def test_row_per_wave_kernel_guards_large_launches(dt, N, D, B):
     special_o = synth.to_storage(torch.tensor([math.nan, math.inf, -math.inf]), dt)
     for k in range(600):
         o[rng.integers(N), rng.integers(B), rng.integers(Hpr), rng.integers(D)] = special_o[k % 3]
-    out, gg = ops.dcp_lse_combine(to_dev(o, dt, DEV), torch.from_numpy(lse).to(DEV), is_lse_base_on_e=False)
+    # out and G inside guarded byte buffers
+    esz = np.dtype(NP_DT[dt]).itemsize
+    nout, nlse, guard = B * Hpr * D * esz, B * Hpr * 4, 4096
+    rng_g = np.random.default_rng(B + Hpr)
+    hout = np.frombuffer(rng_g.bytes(nout + 2 * guard), np.uint8).copy()
+    hlse = np.frombuffer(rng_g.bytes(nlse + 2 * guard), np.uint8).copy()
+    bout, blse = torch.from_numpy(hout).to(DEV), torch.from_numpy(hlse).to(DEV)
+    out_v = bout[guard:guard + nout].view(TORCH_DT[dt]).view(B, Hpr, D)
+    lse_v = blse[guard:guard + nlse].view(torch.float32).view(B, Hpr)
+    out, gg = ops.dcp_lse_combine(to_dev(o, dt, DEV), torch.from_numpy(lse).to(DEV), is_lse_base_on_e=False,
+                                  out=out_v, out_lse=lse_v)
     ref, gr, mag, _ = orc.combine(o, lse, dt, True)
     check_out(decode(to_host(out, dt), dt), ref, mag, dt)
     check_lse(gg.cpu().numpy(), gr)
+    gout, glse = bout.cpu().numpy(), blse.cpu().numpy()
+    for got, host, n in ((gout, hout, nout), (glse, hlse, nlse)):
+        assert np.array_equal(got[:guard], host[:guard]) and np.array_equal(got[guard + n:], host[guard + n:]), \
+            "a store landed outside the output"
 
 
 @pytest.mark.parametrize("dt,N,B,Hpr,D", [

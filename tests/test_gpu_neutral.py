@@ -31,7 +31,7 @@ DEV = torch.device("cuda:0")
     ("fp8", 16, 128, 8, 512, "interleaved"),  # the same launch with two LSE words per wave-step
     ("f32", 2, 7, 4, 64, "interleaved"),      # row kernel (short rows)
     ("f16", 4, 6, 16, 128, "split"),          # split layout
-    ("fp8", 8, 9, 16, 512, "interleaved"),    # fp8: two-LSE stream kernel (516-byte rows)
+    ("fp8", 8, 9, 16, 512, "interleaved"),    # fp8: stream kernel, 516-byte rows (two LSE words in most wave-steps)
     ("fp8", 4, 6, 16, 128, "split"),          # fp8 split layout
 ])
 def test_pack_neutralises_zero_kv_tokens(dt, N, B, Hpr, D, layout):
