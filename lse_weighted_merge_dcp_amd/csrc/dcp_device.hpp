@@ -93,22 +93,14 @@ __device__ __forceinline__ Vec<16> gload16(uint64_t base, uint32_t off) {
     return v;
 }
 
-// V bytes at base + off (V = 16, 8 or 4; 4-byte aligned), as gload16.
-typedef const u32x2_a4 __attribute__((address_space(1))) g_u32x2_a4;
+// V bytes at base + off (V = 16 or 4; 4-byte aligned), as gload16.
 typedef const uint32_t __attribute__((address_space(1))) g_u32;
 template <int V, bool NTL>
 __device__ __forceinline__ Vec<V> gloadv(uint64_t base, uint32_t off) {
     if constexpr (V == 16) {
         return gload16<NTL>(base, off);
-    } else if constexpr (V == 8) {
-        g_u32x2_a4* p = (g_u32x2_a4*)(base + off);
-        u32x2_a4 x;
-        if constexpr (NTL) x = __builtin_nontemporal_load(p); else x = *p;
-        Vec<8> v;
-        v.w[0] = x.x; v.w[1] = x.y;
-        return v;
     } else {
-        static_assert(V == 4, "gloadv: V = 16, 8 or 4");
+        static_assert(V == 4, "gloadv: V = 16 or 4");
         g_u32* p = (g_u32*)(base + off);
         Vec<4> v;
         if constexpr (NTL) v.w[0] = __builtin_nontemporal_load(p); else v.w[0] = *p;
