@@ -39,22 +39,38 @@ def _dt(t: torch.Tensor) -> int:
     return _DTYPE.get(t.dtype, -1)
 
 
-def _stream(t: torch.Tensor):
-    return torch.cuda.current_stream(t.device).cuda_stream
+# The raw HIP stream of a device's current stream, without building a
+# torch.cuda.Stream object per call (a public-API fallback where the direct
+# query is absent).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _invoke(name: str, args: tuple, timing, device: torch.device) -> None:
+def _stream(device: int):
+    if _raw_stream is not None:
+        return _raw_stream(device)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _invoke(name: str, args: tuple, timing, device: int) -> None:
     """Call `name` of libdcpmerge.so with the marshalled arguments, or its
     timed twin of the measurement library when timing events are given, with
     the tensors' device current (the library launches on the current
     device, on that device's stream)."""
-    with torch.cuda.device(device):
+    if device == torch.cuda.current_device():
+        ctx = None
+    else:
+        ctx = torch.cuda.device(device)
+        ctx.__enter__()
+    try:
         if timing is None:
             st = getattr(_lib.lib(), name)(*args)
         else:
             from . import timing as _timing
 
             st = _timing.call_timed(name, args, *timing)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
     _lib.check(st, name)
 
 
@@ -63,25 +79,42 @@ def _require(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
-def _on_gpu(*ts: Optional[torch.Tensor]) -> None:
+def _on_gpu(*ts: Optional[torch.Tensor]) -> int:
+    """The device index all given tensors share (ValueError unless they are
+    device tensors of one device)."""
     dev = None
     for t in ts:
         if t is None:
             continue
-        _require(t.is_cuda, "libdcpmerge works on device tensors only (got %s)" % t.device)
-        _require(dev is None or t.device == dev, "all tensors must be on one device")
-        dev = t.device
+        i = t.get_device()
+        if i < 0:
+            raise ValueError("libdcpmerge works on device tensors only (got %s)" % t.device)
+        if dev is None:
+            dev = i
+        elif i != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
 
 
 def _payload_ok(t: torch.Tensor, name: str) -> None:
-    _require(t.dtype in _DTYPE, "%s: unsupported dtype %s" % (name, t.dtype))
+    if t.dtype not in _DTYPE:
+        raise ValueError("%s: unsupported dtype %s" % (name, t.dtype))
     # (an empty tensor's strides are arbitrary; the call is then a no-op)
-    _require(t.numel() == 0 or t.shape[-1] == 1 or t.stride(-1) == 1,
-             "%s: the last (D) dimension must be contiguous" % name)
+    if not (t.stride(-1) == 1 or t.shape[-1] == 1 or t.numel() == 0):
+        raise ValueError("%s: the last (D) dimension must be contiguous" % name)
 
 
 def _lse_ok(t: torch.Tensor, name: str) -> None:
-    _require(t.dtype == torch.float32, "%s: LSE tensors are float32" % name)
+    if t.dtype != torch.float32:
+        raise ValueError("%s: LSE tensors are float32" % name)
+
+
+def _lead(t: torch.Tensor, nd: int):
+    """Shape and strides of t with a leading R dimension: t's own when it has
+    nd dimensions, else R = 1 with stride 0 (no view is made)."""
+    if t.dim() == nd:
+        return tuple(t.shape), t.stride()
+    return (1,) + tuple(t.shape), (0,) + t.stride()
 
 
 def lse_pack_dim(dtype: torch.dtype) -> int:
@@ -117,37 +150,43 @@ def dcp_pack_a2a_send(out: torch.Tensor, lse: torch.Tensor, dst_o: torch.Tensor,
     kv_len ([B] or [R,B] int32, optional): tokens whose rank-local KV length
     is 0 are sent as the neutral pair (0, -inf) instead of the partial (the
     fixup_zero_kv_rows step of sglang PR #33926 report, 实现拆解 item 3)."""
-    _on_gpu(out, lse, dst_o, dst_lse, kv_len)
-    batched = out.dim() == 4
-    if not batched:
-        out, lse, dst_o, dst_lse = out[None], lse[None], dst_o[None], dst_lse[None]
-        kv_len = kv_len[None] if kv_len is not None else None
-    _require(out.dim() == 4 and lse.dim() == 3 and dst_o.dim() == 5 and dst_lse.dim() == 4,
-             "expected out [B,H,D], lse [B,H], dst_o [N,B,Hpr,D], dst_lse [N,B,Hpr] (optionally with a leading R)")
-    R, B, H, D = out.shape
-    N = dst_o.shape[1]
-    _require(N >= 1 and H % N == 0, "num_heads (%d) must be divisible by the DCP size (%d)" % (H, N))
+    dev = _on_gpu(out, lse, dst_o, dst_lse, kv_len)
+    nd = 4 if out.dim() == 4 else 3
+    if not (out.dim() == nd and lse.dim() == nd - 1 and dst_o.dim() == nd + 1 and dst_lse.dim() == nd):
+        raise ValueError("expected out [B,H,D], lse [B,H], dst_o [N,B,Hpr,D], dst_lse [N,B,Hpr] "
+                         "(optionally with a leading R)")
+    (R, B, H, D), so = _lead(out, 4)
+    N = dst_o.shape[-4]
+    if not (N >= 1 and H % N == 0):
+        raise ValueError("num_heads (%d) must be divisible by the DCP size (%d)" % (H, N))
     Hpr = H // N
-    _require(tuple(lse.shape) == (R, B, H), "lse shape %s != %s" % (tuple(lse.shape), (R, B, H)))
-    _require(tuple(dst_o.shape) == (R, N, B, Hpr, D), "dst_o shape %s != %s" % (tuple(dst_o.shape), (R, N, B, Hpr, D)))
-    _require(tuple(dst_lse.shape) == (R, N, B, Hpr), "dst_lse shape %s" % (tuple(dst_lse.shape),))
-    _require(dst_o.dtype == out.dtype, "dst_o dtype must equal out dtype")
+    lsh, sl = _lead(lse, 3)
+    dsh, do = _lead(dst_o, 5)
+    dlsh, dl = _lead(dst_lse, 4)
+    if lsh != (R, B, H):
+        raise ValueError("lse shape %s != %s" % (tuple(lse.shape), (R, B, H)))
+    if dsh != (R, N, B, Hpr, D):
+        raise ValueError("dst_o shape %s != %s" % (tuple(dst_o.shape), (R, N, B, Hpr, D)))
+    if dlsh != (R, N, B, Hpr):
+        raise ValueError("dst_lse shape %s" % (tuple(dst_lse.shape),))
+    if dst_o.dtype != out.dtype:
+        raise ValueError("dst_o dtype must equal out dtype")
     _payload_ok(out, "out")
     _payload_ok(dst_o, "dst_o")
     _lse_ok(lse, "lse")
     _lse_ok(dst_lse, "dst_lse")
     kl = (0, 0)
     if kv_len is not None:
-        _require(kv_len.dtype == torch.int32 and tuple(kv_len.shape) == (R, B), "kv_len must be int32 [R,B] / [B]")
-        kl = kv_len.stride()
-    so, sl, do, dl = out.stride(), lse.stride(), dst_o.stride(), dst_lse.stride()
+        ksh, kl = _lead(kv_len, 2)
+        if not (kv_len.dtype == torch.int32 and ksh == (R, B) and kv_len.dim() == nd - 2):
+            raise ValueError("kv_len must be int32 [R,B] / [B]")
     _invoke("dcp_pack", (
         out.data_ptr(), so[0], so[1], so[2],
         lse.data_ptr(), sl[0], sl[1], sl[2],
         dst_o.data_ptr(), do[0], do[1], do[2], do[3],
         dst_lse.data_ptr(), dl[0], dl[1], dl[2], dl[3],
         kv_len.data_ptr() if kv_len is not None else None, kl[0], kl[1],
-        R, N, B, H, D, _dt(out), _stream(out)), timing, out.device)
+        R, N, B, H, D, _dt(out), _stream(dev)), timing, dev)
 
 
 def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on_e: bool = True,
@@ -157,39 +196,38 @@ def dcp_lse_combine(recv_o: torch.Tensor, recv_lse: torch.Tensor, is_lse_base_on
     recv_lse [N,B,Hpr].  Returns (out [B,Hpr,D], global LSE [B,Hpr] or None).
     The global LSE is in the input's base.  With a leading R dimension
     (recv_o [R,N,B,Hpr,D]) R merges run at once."""
-    _on_gpu(recv_o, recv_lse, out, out_lse)
+    dev = _on_gpu(recv_o, recv_lse, out, out_lse)
     batched = recv_o.dim() == 5
-    if not batched:
-        recv_o, recv_lse = recv_o[None], recv_lse[None]
-        out = out[None] if out is not None else None
-        out_lse = out_lse[None] if out_lse is not None else None
-    _require(recv_o.dim() == 5 and recv_lse.dim() == 4,
-             "expected recv_o [N,B,Hpr,D] and recv_lse [N,B,Hpr] (optionally with a leading R)")
-    R, N, B, Hpr, D = recv_o.shape
-    _require(tuple(recv_lse.shape) == (R, N, B, Hpr), "recv_lse shape %s" % (tuple(recv_lse.shape),))
+    nd = 5 if batched else 4
+    if not (recv_o.dim() == nd and recv_lse.dim() == nd - 1):
+        raise ValueError("expected recv_o [N,B,Hpr,D] and recv_lse [N,B,Hpr] (optionally with a leading R)")
+    (R, N, B, Hpr, D), ro = _lead(recv_o, 5)
+    rlsh, rl = _lead(recv_lse, 4)
+    if rlsh != (R, N, B, Hpr):
+        raise ValueError("recv_lse shape %s" % (tuple(recv_lse.shape),))
     _payload_ok(recv_o, "recv_o")
     _lse_ok(recv_lse, "recv_lse")
     if out is None:
-        out = torch.empty((R, B, Hpr, D), dtype=recv_o.dtype, device=recv_o.device)
-    _require(tuple(out.shape) == (R, B, Hpr, D) and out.dtype == recv_o.dtype, "bad out tensor")
+        out = torch.empty((R, B, Hpr, D) if batched else (B, Hpr, D), dtype=recv_o.dtype, device=recv_o.device)
+    osh, oo = _lead(out, 4)
+    if not (out.dim() == nd - 1 and osh == (R, B, Hpr, D) and out.dtype == recv_o.dtype):
+        raise ValueError("bad out tensor")
     _payload_ok(out, "out")
     if return_lse and out_lse is None:
-        out_lse = torch.empty((R, B, Hpr), dtype=torch.float32, device=recv_o.device)
+        out_lse = torch.empty((R, B, Hpr) if batched else (B, Hpr), dtype=torch.float32, device=recv_o.device)
+    ol = (0, 0, 0)
     if out_lse is not None:
-        _require(tuple(out_lse.shape) == (R, B, Hpr), "bad out_lse shape")
+        olsh, ol = _lead(out_lse, 3)
+        if not (out_lse.dim() == nd - 2 and olsh == (R, B, Hpr)):
+            raise ValueError("bad out_lse shape")
         _lse_ok(out_lse, "out_lse")
-    ro, rl, oo = recv_o.stride(), recv_lse.stride(), out.stride()
-    ol = out_lse.stride() if out_lse is not None else (0, 0, 0)
     _invoke("dcp_unpack_combine", (
         recv_o.data_ptr(), ro[0], ro[1], ro[2], ro[3],
         recv_lse.data_ptr(), rl[0], rl[1], rl[2], rl[3],
         out.data_ptr(), oo[0], oo[1], oo[2],
         out_lse.data_ptr() if out_lse is not None else None, ol[0], ol[1], ol[2],
         R, N, B, Hpr, D, _dt(recv_o),
-        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(recv_o)), timing, recv_o.device)
-    if not batched:
-        out = out[0]
-        out_lse = out_lse[0] if out_lse is not None else None
+        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(dev)), timing, dev)
     return out, (out_lse if return_lse else None)
 
 
@@ -202,23 +240,27 @@ def cp_lse_combine_inplace(partial: torch.Tensor, lse: torch.Tensor, h0: int = 0
     with nan_to_num(o) * w, and out [T,h1-h0,D] = sum of the held scaled
     partials over heads [h0, h1).  Returns out, or (out, global LSE slice)
     if return_lse.  want_out=False only scales (out is None)."""
-    _on_gpu(partial, lse, out, out_lse)
-    _require(partial.dim() == 4 and lse.dim() == 3, "expected partial [P,T,H,D] and lse [N,T,H]")
+    dev = _on_gpu(partial, lse, out, out_lse)
+    if not (partial.dim() == 4 and lse.dim() == 3):
+        raise ValueError("expected partial [P,T,H,D] and lse [N,T,H]")
     P, T, H, D = partial.shape
     N = lse.shape[0]
     h1 = H if h1 is None else h1
-    _require(tuple(lse.shape) == (N, T, H), "lse shape %s" % (tuple(lse.shape),))
+    if lse.shape != (N, T, H):
+        raise ValueError("lse shape %s" % (tuple(lse.shape),))
     _payload_ok(partial, "partial")
     _lse_ok(lse, "lse")
     if want_out and out is None:
         out = torch.empty((T, max(h1 - h0, 0), D), dtype=partial.dtype, device=partial.device)
     if out is not None:
-        _require(tuple(out.shape) == (T, h1 - h0, D) and out.dtype == partial.dtype, "bad out tensor")
+        if not (out.shape == (T, h1 - h0, D) and out.dtype == partial.dtype):
+            raise ValueError("bad out tensor")
         _payload_ok(out, "out")
     if return_lse and out_lse is None:
         out_lse = torch.empty((T, max(h1 - h0, 0)), dtype=torch.float32, device=partial.device)
     if out_lse is not None:
-        _require(tuple(out_lse.shape) == (T, h1 - h0), "bad out_lse shape")
+        if out_lse.shape != (T, h1 - h0):
+            raise ValueError("bad out_lse shape")
         _lse_ok(out_lse, "out_lse")
     ps, ls = partial.stride(), lse.stride()
     os_ = out.stride() if out is not None else (0, 0, 0)
@@ -230,5 +272,5 @@ def cp_lse_combine_inplace(partial: torch.Tensor, lse: torch.Tensor, h0: int = 0
         out.data_ptr() if out is not None else None, os_[0], os_[1],
         out_lse.data_ptr() if out_lse is not None else None, ols[0], ols[1],
         N, P, rank0, T, H, D, _dt(partial),
-        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(partial)), timing, partial.device)
+        _lib.DCP_LSE_BASE_E if is_lse_base_on_e else _lib.DCP_LSE_BASE_2, _stream(dev)), timing, dev)
     return (out, out_lse) if return_lse else out
