@@ -211,7 +211,19 @@ constexpr uint32_t kStreamChunk = 128;
 // launch (measured on MI355X, two paired runs: one rank's long-context pack
 // at B = 8 2.57 -> 2.31 us, at B = 1 1.96 -> 1.84 us, the DeepSeek-V3 pack
 // 24.6 -> 23.8 us cold, the fp8 decode pack 14.5 -> 13.8 us).
-template <int U, int WPB, bool NTL, bool NTS, uint32_t CH = 0>
+//
+// SLSE (the middle range of launch sizes, 8-wave workgroups): once the
+// payload load has gone out (held there by a scheduling barrier), the
+// wave-step's LSE words come through wave-uniform scalar loads instead (the
+// first at or after dword d0 belongs to row kl, the next, for rows under
+// 1 KB, to row kl + 1).  Measured on MI355X, four paired runs: the
+// DeepSeek-V3-shaped step 5,978 -> 6,118 GB/s with them, the fp8 decode step
+// 4,828 -> 4,890; on the smallest launches the lanes' own loads stay faster
+// (the long-context B = 8 step 3,896 against 3,825), and so do calls with KV
+// lengths, whose length load would queue behind the LSE words (the
+// DeepSeek-V3 step with them 6,044 against 5,992); the largest launches are
+// equal either way.
+template <int U, int WPB, bool NTL, bool NTS, uint32_t CH = 0, bool SLSE = false>
 __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) {
     const uint32_t wave = wave_id();
     const uint32_t lane = threadIdx.x & 63u;
@@ -243,7 +255,19 @@ __global__ __launch_bounds__(64 * WPB) void pack_stream_kernel(const StreamK k) 
         const char* sp = sblk + (int64_t)(has_lse ? base - 1u : base) * 4;
         Vec<16> x = NTL ? vload_stream<16>(sp) : vload<16>(sp);
         uint32_t lw = kNegInfBits;
-        if (has_lse) lw = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + row) * k.sl_H);
+        if constexpr (SLSE) {
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t d0 = s * 256u;
+            const uint32_t kl = fdiv(d0, k.f_Wd);
+            const uint32_t jl = kl * k.Wd + k.Wd - 1u;
+            const char* lrow = k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + kl) * k.sl_H;
+            uint32_t lval = kNegInfBits, lval1 = kNegInfBits;
+            if (kl < k.Hpr && jl >= d0 && jl < d0 + 256u) lval = load_word(lrow);
+            if (k.Wd < 256u && kl + 1u < k.Hpr && jl + k.Wd < d0 + 256u) lval1 = load_word(lrow + k.sl_H);
+            lw = row != kl ? lval1 : lval;
+        } else {
+            if (has_lse) lw = load_word(k.src_lse + r * k.sl_R + b * k.sl_B + (p * k.Hpr + row) * k.sl_H);
+        }
         // A token this rank owns no KV for is sent as the neutral pair.  Its
         // KV length is read after the payload load has gone out, so the two
         // are in flight together and the block's rows are read (in bounds)
@@ -302,6 +326,16 @@ hipError_t launch_stream(const StreamK& k, bool nt_source, bool nt_dest, hipStre
     }
     if (k.nsteps >= kStreamWide) {
         const uint32_t blocks = (k.nsteps + 8 * kStreamU - 1) / (8 * kStreamU);
+        if (k.kv == nullptr) {
+            if (nt_dest)
+                return launch_kernel(pack_stream_kernel<kStreamU, 8, true, true, 0, true>, dim3(blocks), dim3(512),
+                                     stream, k, t);
+            if (nt_source)
+                return launch_kernel(pack_stream_kernel<kStreamU, 8, true, false, 0, true>, dim3(blocks), dim3(512),
+                                     stream, k, t);
+            return launch_kernel(pack_stream_kernel<kStreamU, 8, false, false, 0, true>, dim3(blocks), dim3(512),
+                                 stream, k, t);
+        }
         if (nt_dest)
             return launch_kernel(pack_stream_kernel<kStreamU, 8, true, true>, dim3(blocks), dim3(512), stream, k, t);
         if (nt_source)
