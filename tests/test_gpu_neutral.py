@@ -28,6 +28,7 @@ DEV = torch.device("cuda:0")
     ("bf16", 8, 9, 16, 512, "interleaved"),   # stream kernel, 4-wave workgroups
     ("bf16", 16, 40, 8, 512, "interleaved"),  # stream kernel, 8-wave workgroups (>= 32768 wave-steps)
     ("bf16", 16, 64, 8, 512, "interleaved"),  # stream kernel, XCD-chunked 4-wave workgroups (>= 131072 wave-steps)
+    ("bf16", 16, 50, 8, 512, "interleaved"),  # 8-wave launch with nontemporal loads (100 MiB of source)
     ("fp8", 16, 128, 8, 512, "interleaved"),  # the same launch with two LSE words per wave-step
     ("f32", 2, 7, 4, 64, "interleaved"),      # row kernel (short rows)
     ("f16", 4, 6, 16, 128, "split"),          # split layout

@@ -146,13 +146,16 @@ def test_pack_interleaved_stream_shapes(dt, N, B, Hpr, D):
 # Calls of 131,072 wave-steps and more run in 4-wave workgroups whose XCDs
 # take turns on chunks of 128; the long-context workloads above reach them
 # with nontemporal loads (and stores at B = 512).  These cases reach the same
-# launch with ragged batches, plain loads and rows of 516 bytes.
+# launch with ragged batches, plain loads and rows of 516 bytes, and the
+# 8-wave launch below it (32,768 to 131,071 wave-steps, the LSE words through
+# scalar loads) with nontemporal loads.
 LARGE_SHAPES = [
     ("bf16", 16, 16, 60, 8, 512),   # nontemporal source loads, B = 4 * 15
     ("bf16", 16, 16, 58, 8, 512),   # B = 2 * 29
     ("bf16", 16, 16, 57, 8, 512),   # B odd
     ("bf16", 16, 64, 64, 1, 518),   # Hpr = 1, blocks of 65 chunks, 65 MiB of source: plain loads
     ("f32", 16, 16, 112, 8, 128),   # rows of 516 B: two LSE words in most wave-steps
+    ("bf16", 16, 16, 50, 8, 512),   # 115,200 wave-steps, 100 MiB of source: 8-wave launch with nontemporal loads
 ]
 
 
